@@ -1,0 +1,198 @@
+"""Throughput of the 3D-RoPE attention hot path over one decode window.
+
+One step = one 25-frame decode window: 4 sampling steps x 30 transformer
+blocks = 120 attention calls (12 heads x 10920 tokens x head_dim 128, latent
+grid 7 x 30 x 52), each on its own pre-drawn seeded Q/K/V, all resident in
+HBM before timing starts. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s and % bf16 MFMA peak; ms per 4-step decode window, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="window25_12x128_n10920")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, target_s):
+    """The fp64 oracle on a bounded row sample of one call of the workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from diffusion_transformer_attention_dit_amd import synth
+
+    q, k, v = synth.make_qkv(w, 0, 0, device="cpu")
+    qd, kd, vd = (t.float().numpy().astype(np.float64) for t in (q, k, v))
+    del q, k, v
+    # K rotation of the whole window (once per call) is timed separately.
+    t0 = time.perf_counter()
+    oracle.c_rope_grid(kd, w.grid)
+    rope_s = time.perf_counter() - t0
+    # Calibrate the per-row cost, then size the sample to ~target_s.
+    rows = synth.sample_rows(w.tokens, 4, seed=11)
+    t0 = time.perf_counter()
+    oracle.rope_attention(qd, kd, vd, w.grid, rows=rows)
+    cal = time.perf_counter() - t0 - rope_s
+    per_row = max(cal, 1e-3) / (len(rows) * w.heads)
+    n_rows = int(max(8, min(w.tokens, target_s / per_row / w.heads)))
+    rows = synth.sample_rows(w.tokens, n_rows, seed=12)
+    t0 = time.perf_counter()
+    oracle.rope_attention(qd, kd, vd, w.grid, rows=rows)
+    el = time.perf_counter() - t0
+    attn_s = max(el - rope_s, 1e-9)
+    flops = 4.0 * w.head_dim * w.tokens * len(rows) * w.heads
+    tflops = flops / attn_s / 1e12
+    call_s = w.flops_per_call / (tflops * 1e12) + rope_s
+    return {
+        "value": tflops, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+        "sample": "%d query rows x %d heads of one %s call (%d keys each, fp64); K rotation of "
+                  "the full call %.2f s; %.1f s total" % (len(rows), w.heads, w.name, w.tokens,
+                                                          rope_s, el),
+        "ms_per_window_extrapolated": call_s * w.calls * 1e3,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build carries no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+    import torch
+
+    from diffusion_transformer_attention_dit_amd import native, synth
+    from diffusion_transformer_attention_dit_amd.sampler import WindowDriver
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    native.lib()  # fail loudly if the HIP library is missing
+    w = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    print("bench: drawing %d calls of %s" % (w.calls, w.name), file=sys.stderr, flush=True)
+    drv = WindowDriver(w, device="cuda")
+    # A second handle with kernel events, used for the per-kernel timing of
+    # the same calls.
+    prof = native.Attention(w.heads, w.head_dim, w.grid, flags=native.REGEN_ATTN_PROFILE)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        drv.run_window(stream)
+    torch.cuda.synchronize()
+    print("bench: warmup done", file=sys.stderr, flush=True)
+
+    # ---- timed region: K whole windows -----------------------------------
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        drv.run_window(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(end)
+    ms_per_window = ms_total / args.steps
+    value = drv.flops * args.steps / (ms_total * 1e-3) / 1e12
+    print("bench: timed %d windows, %.2f ms/window" % (args.steps, ms_per_window),
+          file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations from HIP events on the launch stream -------
+    prof.profile_read()
+    for _ in range(max(1, args.steps // 2)):
+        for (q, k, v), i in zip(drv.inputs, range(len(drv.inputs))):
+            prof.forward(q, k, v, out=drv.outs[i & 1], stream=stream)
+    prep_ms, attn_ms, n_calls = prof.profile_read()
+    prof.close()
+    attn_avg_s = attn_ms / n_calls * 1e-3
+    prep_avg_s = prep_ms / n_calls * 1e-3
+    attn_tflops = w.flops_per_call / attn_avg_s / 1e12
+    prep_bytes = 4 * w.heads * w.tokens * w.head_dim * 2  # read K, V; write Kr, Vt
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_window, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "heads": w.heads, "head_dim": w.head_dim,
+            "latent_grid": list(w.grid), "tokens": w.tokens,
+            "calls_per_window": w.calls, "steps_per_window": w.steps, "blocks": w.blocks,
+        },
+        "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "ms_per_window": round(ms_per_window, 3),
+        "ms_per_call": round(ms_total / (args.steps * w.calls), 4),
+        "wall_s_timed": round(wall_s, 3),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(attn_avg_s * 1e6, 2),
+            "launches": n_calls,
+        },
+        "prep_kernel": {
+            "kernel": "rope_k_vt_kernel", "bound": "hbm",
+            "avg_launch_us": round(prep_avg_s * 1e6, 2),
+            "achieved": round(prep_bytes / prep_avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(prep_bytes / prep_avg_s / 1e9 / PEAK_HBM_GBS, 4),
+        },
+    }
+    drv.close()
+    del drv
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 oracle sample on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,370 @@
+// Device kernels of regen_attn for CDNA4 (gfx950).
+//
+// Two kernels make one attention call:
+//
+//  1. rope_k_vt_kernel (HBM-bound pass over K and V): applies the 3D rotary
+//     embedding to K and rounds it to bf16 into a padded row-major copy Kr,
+//     and writes V transposed into Vt, a key-contiguous layout that the P V
+//     matrix product can feed straight from LDS as MFMA operands.
+//  2. attn_fwd_kernel (MFMA-bound): flash-style exact attention. Each wave
+//     owns 32 query rows, rotates its Q rows while loading them (RoPE on
+//     load), then streams K/V tiles through double-buffered LDS and keeps
+//     the online softmax (running max, running sum) in registers.
+//
+// The attention is the one ReGenVC's decoder transformer evaluates over the
+// window's latent tokens (arXiv 2607.28144, blog summary "Methodology - deep
+// read", USP paragraph), kept exact as "Technical innovations" requires; the
+// blocked, online-softmax evaluation follows FlashAttention/FlashAttention-2
+// (index page, "Builds on") but is laid out here for 64-lane wavefronts and
+// 32x32x16 bf16 MFMA.
+//
+// MFMA v_mfma_f32_32x32x16_bf16 operand layout (lane l, c = l % 32,
+// g = l / 32): A supplies row c, k = 8g..8g+7; B supplies column c,
+// k = 8g..8g+7; the 16 fp32 results of lane l are D[row = 8(i/4) + 4g + i%4]
+// [column c], i = 0..15.
+//
+// Attention is computed transposed, S^T = K Q^T, so that a lane's results
+// all belong to ONE query (its column c) and 16 keys: the row max and row
+// sum are in-lane reductions plus one exchange with lane l ^ 32
+// (v_permlane32_swap), and the O^T = V^T P^T product consumes the
+// probabilities straight from registers as its B operand. The key order that
+// the B operand then implies (slot 8g + j <-> key 8(j/4) + 4g + j%4 inside
+// each group of 16) is baked into Vt by the first kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace regen {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPrepKeys = 128;  // keys per rope_k_vt block; workspace padding unit
+constexpr int kVtBlk = 64;      // key slots per Vt block
+
+// Rotary geometry: latent grid, pairs per axis, offsets of each axis' table
+// in the (cos, sin) table. Entry off[a] + pos * pairs[a] + j holds
+// (cos, sin) of pos * base^(-j / pairs[a]).
+struct RopeGeom {
+    int T, H, W;
+    int pairs[3];
+    int off[3];
+};
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to bf16 (round-to-nearest-even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// (cos, sin) for rotary pair i of a token at (t, h, w).
+__device__ __forceinline__ float2 rope_cs(const float2* __restrict__ tab, const RopeGeom& g,
+                                          int i, int t, int h, int w) {
+    int idx;
+    if (i < g.pairs[0]) {
+        idx = g.off[0] + t * g.pairs[0] + i;
+    } else if (i < g.pairs[0] + g.pairs[1]) {
+        idx = g.off[1] + h * g.pairs[1] + (i - g.pairs[0]);
+    } else {
+        idx = g.off[2] + w * g.pairs[2] + (i - g.pairs[0] - g.pairs[1]);
+    }
+    return tab[idx];
+}
+
+// Rotate the 4 pairs held in one 16-byte chunk (8 bf16, pairs i0..i0+3).
+__device__ __forceinline__ uint4 rope_chunk(uint4 in, const float2* __restrict__ tab,
+                                            const RopeGeom& g, int i0, int t, int h, int w) {
+    uint32_t src[4] = {in.x, in.y, in.z, in.w};
+    uint32_t dst[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        float2 cs = rope_cs(tab, g, i0 + p, t, h, w);
+        float x = bf_lo(src[p]), y = bf_hi(src[p]);
+        float xr = x * cs.x - y * cs.y;
+        float yr = x * cs.y + y * cs.x;
+        dst[p] = pack_bf16(xr, yr);
+    }
+    return make_uint4(dst[0], dst[1], dst[2], dst[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1: K rotation + V transpose. Grid (Npad / 128, heads), 256 threads.
+//   Kr : [heads][Npad][D] bf16, rotated, rows >= N zero.
+//   Vt : [heads][Npad/64][D][64] bf16; inside each group of 16 slots, slot
+//        8g + j holds key 8(j/4) + 4g + j%4 of that group; keys >= N zero.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void rope_k_vt_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ kr,
+    uint16_t* __restrict__ vt, const float2* __restrict__ tab, RopeGeom geo, int N, int Npad) {
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    const int tile = blockIdx.x, hd = blockIdx.y;
+    const int n0 = tile * kPrepKeys;
+    const int HW = geo.H * geo.W;
+
+    for (int cid = threadIdx.x; cid < kPrepKeys * CPR; cid += 256) {
+        const int r = cid / CPR, c = cid % CPR;
+        const int n = n0 + r;
+        uint4 out = make_uint4(0, 0, 0, 0);
+        if (n < N) {
+            uint4 in = *reinterpret_cast<const uint4*>(k + ((size_t)hd * N + n) * D + c * 8);
+            const int t = n / HW, h = (n / geo.W) % geo.H, w = n % geo.W;
+            out = rope_chunk(in, tab, geo, c * 4, t, h, w);
+        }
+        *reinterpret_cast<uint4*>(kr + ((size_t)hd * Npad + n) * D + c * 8) = out;
+    }
+
+    // V: each thread gathers the 8 keys of one 8-slot output chunk for one
+    // column chunk of 8 head dims, transposes the 8 x 8 block in registers
+    // and writes 8 rows of 16 bytes. Threads with consecutive g write one
+    // 128-byte Vt row together.
+    constexpr int COMBOS = 16 * CPR;
+    const int tid = threadIdx.x;
+    if (tid < COMBOS) {
+        const int g = tid % 8, rest = tid / 8;
+        const int blk = rest % 2, c = rest / 2;
+        const int G = blk * 4 + g / 2, hh = g % 2;
+        uint32_t a[8][4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int key = n0 + G * 16 + (j / 4) * 8 + hh * 4 + (j % 4);
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (key < N) x = *reinterpret_cast<const uint4*>(v + ((size_t)hd * N + key) * D + c * 8);
+            a[j][0] = x.x; a[j][1] = x.y; a[j][2] = x.z; a[j][3] = x.w;
+        }
+        uint16_t* dst = vt + ((size_t)(hd * (Npad / kVtBlk) + tile * 2 + blk) * D + c * 8) * kVtBlk + g * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t wv[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                uint32_t x0 = a[2 * m][e / 2], x1 = a[2 * m + 1][e / 2];
+                wv[m] = (e & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+            }
+            *reinterpret_cast<uint4*>(dst + e * kVtBlk) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+    }
+}
+
+// Logical block id with consecutive ids on one XCD. Blocks are dispatched
+// round-robin over the 8 XCDs (block b runs on XCD b % 8); this maps each
+// XCD's blocks onto one contiguous range of logical ids, so that the blocks
+// sharing an XCD's L2 work on the same head's K/V.
+__device__ __forceinline__ int xcd_remap(int b, int G) {
+    const int per = G / 8, rem = G % 8, x = b % 8, loc = b / 8;
+    return (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: attention. Grid heads * ceil(N / (32 NW)), NW * 64 threads.
+// ---------------------------------------------------------------------------
+template <int D, int BN, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kr,
+    const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, const float2* __restrict__ tab,
+    RopeGeom geo, int N, int Npad, int n_qtiles, float c2 /* sm_scale * log2(e) */) {
+    static_assert(D == 64 || D == 128, "head_dim");
+    static_assert(BN == 64 || BN == 128, "key tile");
+    constexpr int T = NW * 64;
+    constexpr int KSTR = D * 2 + 16;   // LDS bytes per K row (16 B pad: conflict-free b128 reads)
+    constexpr int VSTR = BN * 2 + 16;  // LDS bytes per Vt row
+    constexpr int KBYTES = BN * KSTR, VBYTES = D * VSTR;
+    constexpr int KCH = BN * D / 8, VCH = D * BN / 8;  // 16-byte chunks per tile
+    constexpr int KPT = KCH / T, VPT = VCH / T;
+    static_assert(KCH % T == 0 && VCH % T == 0, "tile/threads");
+    constexpr float kLazy = 8.0f;  // rescale only when the max grows by > 2^8
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * (KBYTES + VBYTES)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int hd = L / n_qtiles, qt = L % n_qtiles;
+    const int qrow = qt * (NW * 32) + wave * 32 + col;
+
+    // ---- Q: load this lane's half-rows and rotate them (RoPE on load) ----
+    bf16x8 qf[D / 16];
+    {
+        const int HW = geo.H * geo.W;
+        const int qn = qrow < N ? qrow : 0;
+        const int t = qn / HW, h = (qn / geo.W) % geo.H, w = qn % geo.W;
+        const uint16_t* qp = q + ((size_t)hd * N + qn) * D + half * 8;
+#pragma unroll
+        for (int kb = 0; kb < D / 16; ++kb) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (qrow < N) {
+                x = *reinterpret_cast<const uint4*>(qp + kb * 16);
+                x = rope_chunk(x, tab, geo, kb * 8 + half * 4, t, h, w);
+            }
+            qf[kb] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
+    float m_run = -INFINITY;  // running max in the exp2 domain (scaled)
+    float l_run = 0.0f;       // this lane's partial row sum
+
+    const int nt = (N + BN - 1) / BN;
+    const char* kbase = reinterpret_cast<const char*>(kr + (size_t)hd * Npad * D);
+    const char* vbase = reinterpret_cast<const char*>(vt + (size_t)hd * Npad * D);
+
+    uint4 kreg[KPT], vreg[VPT];
+    auto gload = [&](int j) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int cid = tid + i * T;
+            const int r = cid / (D / 8), c = cid % (D / 8);
+            kreg[i] = *reinterpret_cast<const uint4*>(kbase + ((size_t)(j * BN + r) * D + c * 8) * 2);
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int cid = tid + i * T;
+            const int blk = cid / (D * 8), rem = cid % (D * 8);
+            const int d = rem / 8, g = rem % 8;
+            vreg[i] = *reinterpret_cast<const uint4*>(
+                vbase + ((size_t)((j * BN / kVtBlk + blk) * D + d) * kVtBlk + g * 8) * 2);
+        }
+    };
+    auto lstore = [&](int buf) {
+        char* ks = smem + buf * (KBYTES + VBYTES);
+        char* vs = ks + KBYTES;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int cid = tid + i * T;
+            const int r = cid / (D / 8), c = cid % (D / 8);
+            *reinterpret_cast<uint4*>(ks + r * KSTR + c * 16) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int cid = tid + i * T;
+            const int blk = cid / (D * 8), rem = cid % (D * 8);
+            const int d = rem / 8, g = rem % 8;
+            *reinterpret_cast<uint4*>(vs + d * VSTR + (blk * kVtBlk + g * 8) * 2) = vreg[i];
+        }
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+
+    for (int j = 0; j < nt; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < nt) gload(j + 1);
+        const char* ks = smem + buf * (KBYTES + VBYTES);
+        const char* vs = ks + KBYTES;
+
+        // S^T = K Q^T for this tile: BN keys x 32 queries.
+        f32x16 s[BN / 32];
+#pragma unroll
+        for (int kk = 0; kk < BN / 32; ++kk) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kk][i] = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < D / 16; ++kb) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    ks + (kk * 32 + col) * KSTR + (kb * 16 + half * 8) * 2);
+                s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s[kk], 0, 0, 0);
+            }
+        }
+
+        // Keys past the end of the sequence get -inf (never zero-padding).
+        if (j == nt - 1 && (N % BN) != 0) {
+#pragma unroll
+            for (int kk = 0; kk < BN / 32; ++kk)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = j * BN + kk * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+                    if (key >= N) s[kk][i] = -INFINITY;
+                }
+        }
+
+        // Row max: in-lane over this lane's keys, then with lane ^ 32.
+        float mx = s[0][0];
+#pragma unroll
+        for (int kk = 0; kk < BN / 32; ++kk)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kk][i]);
+        {
+            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float m_new = mx * c2;
+        // Lazy rescale: the final O / l is exact for any reference value m_run
+        // not below the true max by more than kLazy (P stays <= 2^kLazy).
+        if (m_new > m_run + kLazy) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        }
+
+        // P = exp2(S * c2 - m_run), bf16 for the second product.
+        bf16x8 p[BN / 16];
+#pragma unroll
+        for (int kk = 0; kk < BN / 32; ++kk)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                uint32_t w4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk][hb * 8 + 2 * e], c2, -m_run));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk][hb * 8 + 2 * e + 1], c2, -m_run));
+                    l_run += e0 + e1;
+                    w4[e] = pack_bf16(e0, e1);
+                }
+                p[kk * 2 + hb] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+            }
+
+        // O^T += V^T P^T.
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int kq = 0; kq < BN / 16; ++kq) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    vs + (db * 32 + col) * VSTR + (kq * 16 + half * 8) * 2);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kq], acc[db], 0, 0, 0);
+            }
+
+        if (j + 1 < nt) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = O^T / l, bf16 ----
+    {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+                                                   false, false);
+        const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const float inv = 1.0f / l_tot;
+        if (qrow < N) {
+            uint16_t* op = o + ((size_t)hd * N + qrow) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d0 = db * 32 + g4 * 8 + half * 4;
+                    uint2 w2;
+                    w2.x = pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv);
+                    w2.y = pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv);
+                    *reinterpret_cast<uint2*>(op + d0) = w2;
+                }
+        }
+    }
+}
+
+}  // namespace regen

@@ -1,0 +1,358 @@
+// Host side of regen_attn: argument checking, rotary tables, workspace,
+// launches. The C ABI is declared (with its contract) in include/regen_attn.h.
+#include "regen_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr uint32_t kKnownFlags = REGEN_ATTN_NO_ROPE | REGEN_ATTN_PROFILE;
+constexpr int64_t kMaxTokens = int64_t(1) << 30;
+
+thread_local std::string g_last_error;
+
+// Live handles. A handle is looked up here before it is dereferenced, so a
+// destroyed or foreign pointer is rejected instead of being read.
+std::mutex g_live_mu;
+std::unordered_set<const void*> g_live;
+
+bool is_live(const void* h) {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    return g_live.count(h) != 0;
+}
+
+regen_status fail(regen_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+regen_status fail_hip(hipError_t e, const char* what) {
+    std::string m = what;
+    m += ": ";
+    m += hipGetErrorString(e);
+    return fail(REGEN_ERR_HIP, m);
+}
+
+// Fully resolved problem: defaults applied, all fields checked.
+struct Problem {
+    int heads, head_dim, T, H, W;
+    int pairs[3];
+    double base;
+    float scale;
+    uint32_t flags;
+    int64_t tokens, tokens_pad;
+};
+
+regen_status resolve(const regen_attn_desc* d, Problem* p) {
+    if (!d) return fail(REGEN_ERR_INVALID_ARGUMENT, "desc is NULL");
+    if (d->struct_size != sizeof(regen_attn_desc))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "desc->struct_size does not match this library");
+    if (d->heads < 1) return fail(REGEN_ERR_INVALID_ARGUMENT, "heads must be >= 1");
+    if (d->grid_t < 1 || d->grid_h < 1 || d->grid_w < 1)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "grid_t, grid_h, grid_w must be >= 1");
+    if (d->flags & ~kKnownFlags) return fail(REGEN_ERR_INVALID_ARGUMENT, "unknown flag bits");
+    if (!(d->rope_base >= 0.0f) || !std::isfinite(d->rope_base))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "rope_base must be > 0 (or 0 for the default)");
+    if (!(d->sm_scale >= 0.0f) || !std::isfinite(d->sm_scale))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "sm_scale must be > 0 (or 0 for the default)");
+    if (d->head_dim <= 0 || d->head_dim % 2 != 0)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "head_dim must be a positive even number");
+    const int half = d->head_dim / 2;
+    int pt = d->pairs_t, ph = d->pairs_h, pw = d->pairs_w;
+    if (pt == 0 && ph == 0 && pw == 0) {
+        ph = pw = half / 3;
+        pt = half - 2 * ph;
+    } else if (pt < 1 || ph < 1 || pw < 1 || pt + ph + pw != half) {
+        return fail(REGEN_ERR_INVALID_ARGUMENT,
+                    "pairs_t/h/w must each be >= 1 and sum to head_dim/2 (or all be 0)");
+    }
+    const int64_t tokens = int64_t(d->grid_t) * d->grid_h * d->grid_w;
+    if (tokens > kMaxTokens) return fail(REGEN_ERR_INVALID_ARGUMENT, "too many tokens (> 2^30)");
+    if (int64_t(d->heads) * tokens * d->head_dim > (int64_t(1) << 40))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "tensor too large");
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(REGEN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    p->heads = d->heads;
+    p->head_dim = d->head_dim;
+    p->T = d->grid_t;
+    p->H = d->grid_h;
+    p->W = d->grid_w;
+    p->pairs[0] = pt;
+    p->pairs[1] = ph;
+    p->pairs[2] = pw;
+    p->base = d->rope_base > 0.0f ? double(d->rope_base) : 10000.0;
+    p->scale = d->sm_scale > 0.0f ? d->sm_scale : float(1.0 / std::sqrt(double(d->head_dim)));
+    p->flags = d->flags;
+    p->tokens = tokens;
+    p->tokens_pad = (tokens + regen::kPrepKeys - 1) / regen::kPrepKeys * regen::kPrepKeys;
+    return REGEN_OK;
+}
+
+size_t workspace_bytes(const Problem& p) {
+    // Kr and Vt, bf16 each.
+    return size_t(2) * size_t(p.heads) * size_t(p.tokens_pad) * size_t(p.head_dim) * 2;
+}
+
+}  // namespace
+
+// Events of one profiled forward: before the first kernel, between the two,
+// after the second.
+struct ProfRecord {
+    hipEvent_t ev[3];
+};
+
+struct regen_attn {
+    int device;
+    std::vector<ProfRecord> prof_pending;  // recorded, not yet read
+    std::vector<ProfRecord> prof_free;     // created, reusable
+    Problem p;
+    regen::RopeGeom geo;
+    float2* d_tab;   // rotary (cos, sin) per axis
+    uint16_t* d_kr;  // workspace: rotated K
+    uint16_t* d_vt;  // workspace: transposed V
+};
+
+extern "C" {
+
+const char* regen_attn_status_string(regen_status s) {
+    switch (s) {
+        case REGEN_OK: return "REGEN_OK";
+        case REGEN_ERR_INVALID_ARGUMENT: return "REGEN_ERR_INVALID_ARGUMENT";
+        case REGEN_ERR_UNSUPPORTED: return "REGEN_ERR_UNSUPPORTED";
+        case REGEN_ERR_NO_DEVICE: return "REGEN_ERR_NO_DEVICE";
+        case REGEN_ERR_OUT_OF_MEMORY: return "REGEN_ERR_OUT_OF_MEMORY";
+        case REGEN_ERR_HIP: return "REGEN_ERR_HIP";
+    }
+    return "REGEN_ERR_UNKNOWN";
+}
+
+const char* regen_attn_last_error(void) { return g_last_error.c_str(); }
+
+size_t regen_attn_workspace_size(const regen_attn_desc* desc) {
+    Problem p;
+    std::string saved = g_last_error;
+    regen_status s = resolve(desc, &p);
+    g_last_error = saved;
+    return s == REGEN_OK ? workspace_bytes(p) : 0;
+}
+
+regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
+    g_last_error.clear();
+    if (!out) return fail(REGEN_ERR_INVALID_ARGUMENT, "out is NULL");
+    *out = nullptr;
+    Problem p;
+    regen_status s = resolve(desc, &p);
+    if (s != REGEN_OK) return s;
+
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count < 1) {
+        (void)hipGetLastError();
+        return fail(REGEN_ERR_NO_DEVICE, "no HIP device is available");
+    }
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return fail_hip(e, "hipGetDevice");
+    hipDeviceProp_t prop;
+    if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess)
+        return fail_hip(e, "hipGetDeviceProperties");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(REGEN_ERR_UNSUPPORTED,
+                    std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950");
+
+    // Rotary tables in fp64, stored as fp32 (cos, sin).
+    regen::RopeGeom geo;
+    geo.T = p.T;
+    geo.H = p.H;
+    geo.W = p.W;
+    const int extent[3] = {p.T, p.H, p.W};
+    int off = 0;
+    for (int a = 0; a < 3; ++a) {
+        geo.pairs[a] = p.pairs[a];
+        geo.off[a] = off;
+        off += extent[a] * p.pairs[a];
+    }
+    std::vector<float2> tab(off);
+    const bool rope = !(p.flags & REGEN_ATTN_NO_ROPE);
+    for (int a = 0; a < 3; ++a)
+        for (int pos = 0; pos < extent[a]; ++pos)
+            for (int j = 0; j < p.pairs[a]; ++j) {
+                const double theta = std::pow(p.base, -double(j) / double(p.pairs[a]));
+                const double phi = double(pos) * theta;
+                float2 cs;
+                cs.x = rope ? float(std::cos(phi)) : 1.0f;
+                cs.y = rope ? float(std::sin(phi)) : 0.0f;
+                tab[geo.off[a] + pos * p.pairs[a] + j] = cs;
+            }
+
+    regen_attn* h = new (std::nothrow) regen_attn();
+    if (!h) return fail(REGEN_ERR_OUT_OF_MEMORY, "host allocation of the handle failed");
+    h->device = dev;
+    h->p = p;
+    h->geo = geo;
+    h->d_tab = nullptr;
+    h->d_kr = h->d_vt = nullptr;
+
+    const size_t tab_bytes = tab.size() * sizeof(float2);
+    const size_t half_ws = workspace_bytes(p) / 2;
+    auto cleanup = [&]() {
+        if (h->d_tab) (void)hipFree(h->d_tab);
+        if (h->d_kr) (void)hipFree(h->d_kr);
+        if (h->d_vt) (void)hipFree(h->d_vt);
+        delete h;
+    };
+    if ((e = hipMalloc(&h->d_tab, tab_bytes)) != hipSuccess ||
+        (e = hipMalloc(&h->d_kr, half_ws)) != hipSuccess ||
+        (e = hipMalloc(&h->d_vt, half_ws)) != hipSuccess) {
+        (void)hipGetLastError();
+        cleanup();
+        return fail(e == hipErrorOutOfMemory ? REGEN_ERR_OUT_OF_MEMORY : REGEN_ERR_HIP,
+                    std::string("device allocation failed: ") + hipGetErrorString(e));
+    }
+    if ((e = hipMemcpy(h->d_tab, tab.data(), tab_bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+        cleanup();
+        return fail_hip(e, "hipMemcpy of the rotary table");
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_live_mu);
+        g_live.insert(h);
+    }
+    *out = h;
+    return REGEN_OK;
+}
+
+regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, const void* v,
+                                void* o, void* stream) {
+    g_last_error.clear();
+    if (!h || !is_live(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is NULL or not live");
+    if (!q || !k || !v || !o) return fail(REGEN_ERR_INVALID_ARGUMENT, "q, k, v, o must be non-NULL");
+    const uintptr_t ptrs[4] = {uintptr_t(q), uintptr_t(k), uintptr_t(v), uintptr_t(o)};
+    for (uintptr_t a : ptrs)
+        if (a % 16 != 0) return fail(REGEN_ERR_INVALID_ARGUMENT, "q, k, v, o must be 16-byte aligned");
+    const Problem& p = h->p;
+    const uintptr_t bytes = uintptr_t(p.heads) * uintptr_t(p.tokens) * uintptr_t(p.head_dim) * 2;
+    for (int i = 0; i < 3; ++i)
+        if (ptrs[3] < ptrs[i] + bytes && ptrs[i] < ptrs[3] + bytes)
+            return fail(REGEN_ERR_INVALID_ARGUMENT, "o overlaps q, k or v");
+
+    int cur = -1;
+    hipError_t ge = hipGetDevice(&cur);
+    if (ge != hipSuccess) return fail_hip(ge, "hipGetDevice");
+    if (cur != h->device)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "the current HIP device is not the handle's device");
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int N = int(p.tokens), Npad = int(p.tokens_pad);
+    const float c2 = p.scale * 1.4426950408889634f;
+
+    dim3 pgrid(unsigned(Npad / regen::kPrepKeys), unsigned(p.heads));
+    constexpr int NW = 4, BN = 64;
+    const int n_qtiles = (N + NW * 32 - 1) / (NW * 32);
+    const unsigned agrid = unsigned(n_qtiles) * unsigned(p.heads);
+    const uint16_t* q16 = static_cast<const uint16_t*>(q);
+    const uint16_t* k16 = static_cast<const uint16_t*>(k);
+    const uint16_t* v16 = static_cast<const uint16_t*>(v);
+    uint16_t* o16 = static_cast<uint16_t*>(o);
+
+    ProfRecord rec{};
+    const bool prof = (p.flags & REGEN_ATTN_PROFILE) != 0;
+    if (prof) {
+        if (!h->prof_free.empty()) {
+            rec = h->prof_free.back();
+            h->prof_free.pop_back();
+        } else {
+            for (int i = 0; i < 3; ++i) {
+                hipError_t ee = hipEventCreate(&rec.ev[i]);
+                if (ee != hipSuccess) {
+                    for (int j = 0; j < i; ++j) (void)hipEventDestroy(rec.ev[j]);
+                    return fail_hip(ee, "hipEventCreate");
+                }
+            }
+        }
+        (void)hipEventRecord(rec.ev[0], st);
+    }
+    auto between = [&]() {
+        if (prof) (void)hipEventRecord(rec.ev[1], st);
+    };
+
+    if (p.head_dim == 128) {
+        hipLaunchKernelGGL(regen::rope_k_vt_kernel<128>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
+                           h->d_vt, h->d_tab, h->geo, N, Npad);
+        between();
+        hipLaunchKernelGGL((regen::attn_fwd_kernel<128, BN, NW>), dim3(agrid), dim3(NW * 64), 0, st,
+                           q16, h->d_kr, h->d_vt, o16, h->d_tab, h->geo, N, Npad, n_qtiles, c2);
+    } else {
+        hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
+                           h->d_vt, h->d_tab, h->geo, N, Npad);
+        between();
+        hipLaunchKernelGGL((regen::attn_fwd_kernel<64, BN, NW>), dim3(agrid), dim3(NW * 64), 0, st,
+                           q16, h->d_kr, h->d_vt, o16, h->d_tab, h->geo, N, Npad, n_qtiles, c2);
+    }
+    hipError_t e = hipGetLastError();
+    if (prof) {
+        (void)hipEventRecord(rec.ev[2], st);
+        h->prof_pending.push_back(rec);
+    }
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    return REGEN_OK;
+}
+
+regen_status regen_attn_profile_read(regen_attn_t h, double* prep_ms, double* attn_ms,
+                                     int64_t* calls) {
+    g_last_error.clear();
+    if (!h || !is_live(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is NULL or not live");
+    if (!(h->p.flags & REGEN_ATTN_PROFILE))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "handle was created without REGEN_ATTN_PROFILE");
+    double tp = 0.0, ta = 0.0;
+    int64_t n = 0;
+    regen_status st = REGEN_OK;
+    for (ProfRecord& r : h->prof_pending) {
+        float a = 0.0f, b = 0.0f;
+        hipError_t e = hipEventSynchronize(r.ev[2]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&a, r.ev[0], r.ev[1]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&b, r.ev[1], r.ev[2]);
+        if (e != hipSuccess && st == REGEN_OK) st = fail_hip(e, "profile events");
+        tp += a;
+        ta += b;
+        ++n;
+        h->prof_free.push_back(r);
+    }
+    h->prof_pending.clear();
+    if (prep_ms) *prep_ms += tp;
+    if (attn_ms) *attn_ms += ta;
+    if (calls) *calls += n;
+    return st;
+}
+
+regen_status regen_attn_destroy(regen_attn_t h) {
+    g_last_error.clear();
+    if (!h) return REGEN_OK;
+    {
+        std::lock_guard<std::mutex> lk(g_live_mu);
+        if (!g_live.erase(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is not live");
+    }
+    int cur = 0;
+    const bool switched = hipGetDevice(&cur) == hipSuccess && cur != h->device &&
+                          hipSetDevice(h->device) == hipSuccess;
+    (void)hipFree(h->d_tab);
+    (void)hipFree(h->d_kr);
+    (void)hipFree(h->d_vt);
+    for (auto* list : {&h->prof_pending, &h->prof_free})
+        for (ProfRecord& r : *list)
+            for (hipEvent_t ev : r.ev) (void)hipEventDestroy(ev);
+    if (switched) (void)hipSetDevice(cur);
+    delete h;
+    return REGEN_OK;
+}
+
+}  // extern "C"

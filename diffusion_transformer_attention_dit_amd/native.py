@@ -1,0 +1,198 @@
+"""ctypes binding of the C ABI in include/regen_attn.h (argument marshalling only).
+
+Every computation happens in the HIP library ``libregen_attn.so``; there is
+no fallback. If the library is missing, loading fails loudly with the build
+command to run.
+"""
+import ctypes
+import os
+
+from . import build as _build
+
+REGEN_OK = 0
+REGEN_ERR_INVALID_ARGUMENT = 1
+REGEN_ERR_UNSUPPORTED = 2
+REGEN_ERR_NO_DEVICE = 3
+REGEN_ERR_OUT_OF_MEMORY = 4
+REGEN_ERR_HIP = 5
+
+REGEN_ATTN_NO_ROPE = 0x1
+REGEN_ATTN_PROFILE = 0x2
+
+# Names the header declares; the CPU tests check the library exports each.
+EXPORTS = (
+    "regen_attn_create",
+    "regen_attn_forward",
+    "regen_attn_destroy",
+    "regen_attn_status_string",
+    "regen_attn_last_error",
+    "regen_attn_workspace_size",
+    "regen_attn_profile_read",
+)
+
+
+class regen_attn_desc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("grid_t", ctypes.c_int32),
+        ("grid_h", ctypes.c_int32),
+        ("grid_w", ctypes.c_int32),
+        ("pairs_t", ctypes.c_int32),
+        ("pairs_h", ctypes.c_int32),
+        ("pairs_w", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+        ("sm_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+def make_desc(heads, head_dim, grid, pairs=(0, 0, 0), rope_base=0.0, sm_scale=0.0, flags=0):
+    d = regen_attn_desc()
+    d.struct_size = ctypes.sizeof(regen_attn_desc)
+    d.heads, d.head_dim = int(heads), int(head_dim)
+    d.grid_t, d.grid_h, d.grid_w = (int(x) for x in grid)
+    d.pairs_t, d.pairs_h, d.pairs_w = (int(x) for x in pairs)
+    d.rope_base, d.sm_scale, d.flags = float(rope_base), float(sm_scale), int(flags)
+    return d
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded HIP library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_build.LIB):
+        raise RuntimeError(
+            "libregen_attn.so is not built; run `python -m diffusion_transformer_attention_dit_amd.build`"
+            " (or __graft_entry__.build())")
+    L = ctypes.CDLL(_build.LIB)
+    vp = ctypes.c_void_p
+    L.regen_attn_create.argtypes = [ctypes.POINTER(regen_attn_desc), ctypes.POINTER(vp)]
+    L.regen_attn_create.restype = ctypes.c_int
+    L.regen_attn_forward.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.regen_attn_forward.restype = ctypes.c_int
+    L.regen_attn_destroy.argtypes = [vp]
+    L.regen_attn_destroy.restype = ctypes.c_int
+    L.regen_attn_status_string.argtypes = [ctypes.c_int]
+    L.regen_attn_status_string.restype = ctypes.c_char_p
+    L.regen_attn_last_error.argtypes = []
+    L.regen_attn_last_error.restype = ctypes.c_char_p
+    L.regen_attn_workspace_size.argtypes = [ctypes.POINTER(regen_attn_desc)]
+    L.regen_attn_workspace_size.restype = ctypes.c_size_t
+    L.regen_attn_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int64)]
+    L.regen_attn_profile_read.restype = ctypes.c_int
+    _LIB = L
+    return L
+
+
+class RegenAttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = "%s failed: %s (%s)" % (where, regen_attn_status_string(status), regen_attn_last_error())
+        super().__init__(msg)
+
+
+# ---- the C functions, same names -------------------------------------------
+
+def regen_attn_create(desc):
+    """Returns (status, handle); handle is None on failure."""
+    h = ctypes.c_void_p()
+    s = lib().regen_attn_create(ctypes.byref(desc) if desc is not None else None, ctypes.byref(h))
+    return s, (h.value if s == REGEN_OK else None)
+
+
+def regen_attn_forward(handle, q, k, v, o, stream):
+    """q, k, v, o, stream are integer device addresses / a hipStream_t value."""
+    return lib().regen_attn_forward(handle, q, k, v, o, stream)
+
+
+def regen_attn_destroy(handle):
+    return lib().regen_attn_destroy(handle)
+
+
+def regen_attn_status_string(status):
+    return lib().regen_attn_status_string(int(status)).decode()
+
+
+def regen_attn_last_error():
+    return lib().regen_attn_last_error().decode()
+
+
+def regen_attn_workspace_size(desc):
+    return lib().regen_attn_workspace_size(ctypes.byref(desc) if desc is not None else None)
+
+
+def regen_attn_profile_read(handle):
+    """Returns (status, prep_ms, attn_ms, calls) accumulated since the last read."""
+    a, b, n = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_int64(0)
+    s = lib().regen_attn_profile_read(handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(n))
+    return s, a.value, b.value, n.value
+
+
+# ---- a small convenience wrapper over torch tensors ------------------------
+
+class Attention:
+    """One problem shape on the current device. torch supplies memory and the
+    stream only; the call enqueues the library's kernels."""
+
+    def __init__(self, heads, head_dim, grid, pairs=(0, 0, 0), rope_base=0.0, sm_scale=0.0,
+                 flags=0):
+        self.heads, self.head_dim, self.grid = int(heads), int(head_dim), tuple(grid)
+        self.tokens = self.grid[0] * self.grid[1] * self.grid[2]
+        self.desc = make_desc(heads, head_dim, grid, pairs, rope_base, sm_scale, flags)
+        s, h = regen_attn_create(self.desc)
+        if s != REGEN_OK:
+            raise RegenAttnError(s, "regen_attn_create")
+        self.handle = h
+
+    def _check(self, t, name):
+        import torch
+        shape = (self.heads, self.tokens, self.head_dim)
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous bf16 device tensor" % name)
+        if tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+
+    def forward(self, q, k, v, out=None, stream=None):
+        import torch
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            self._check(t, n)
+        if out is None:
+            out = torch.empty_like(q)
+        self._check(out, "out")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        s = regen_attn_forward(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               out.data_ptr(), stream.cuda_stream)
+        if s != REGEN_OK:
+            raise RegenAttnError(s, "regen_attn_forward")
+        return out
+
+    __call__ = forward
+
+    def profile_read(self):
+        """(prep_ms, attn_ms, calls) since the last read; needs REGEN_ATTN_PROFILE."""
+        s, a, b, n = regen_attn_profile_read(self.handle)
+        if s != REGEN_OK:
+            raise RegenAttnError(s, "regen_attn_profile_read")
+        return a, b, n
+
+    def close(self):
+        if self.handle is not None:
+            s = regen_attn_destroy(self.handle)
+            self.handle = None
+            if s != REGEN_OK:
+                raise RegenAttnError(s, "regen_attn_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

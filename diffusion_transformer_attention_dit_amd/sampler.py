@@ -1,0 +1,48 @@
+"""Four-step sampler driver: one attention call per transformer block per
+sampling step over one decode window.
+
+The ReGenVC decoder is distilled to four sampling steps (arXiv 2607.28144,
+blog summary "Key findings" and "Methodology - deep read"); each step runs
+every block of the diffusion transformer once, and each block attends over
+the window's latent tokens. Without trained weights, each (step, block) call
+gets its own fresh seeded Q/K/V, drawn before timing starts.
+"""
+import torch
+
+from . import synth
+from .native import Attention
+
+
+class WindowDriver:
+    """Holds the library handle, the pre-drawn inputs of every call of one
+    window and a pair of output buffers (alternating, as consecutive blocks
+    would)."""
+
+    def __init__(self, workload: synth.Workload, device="cuda", base_seed=0, steps=None,
+                 blocks=None):
+        self.w = workload
+        self.steps = steps if steps is not None else workload.steps
+        self.blocks = blocks if blocks is not None else workload.blocks
+        self.attn = Attention(workload.heads, workload.head_dim, workload.grid)
+        self.inputs = [synth.make_qkv(workload, s, b, device=device, base_seed=base_seed)
+                       for s in range(self.steps) for b in range(self.blocks)]
+        self.outs = [torch.empty_like(self.inputs[0][0]) for _ in range(2)]
+
+    @property
+    def calls(self):
+        return self.steps * self.blocks
+
+    @property
+    def flops(self):
+        return self.calls * self.w.flops_per_call
+
+    def run_window(self, stream=None):
+        """Enqueue all steps x blocks attention calls on one stream."""
+        for i, (q, k, v) in enumerate(self.inputs):
+            self.attn.forward(q, k, v, out=self.outs[i & 1], stream=stream)
+
+    def output_of(self, call):
+        return self.outs[call & 1]
+
+    def close(self):
+        self.attn.close()

@@ -1,0 +1,161 @@
+/*
+ * regen_attn: 3D-RoPE exact self-attention for the ReGenVC diffusion
+ * transformer decoder, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation. The ReGenVC decoder is a four-step distilled diffusion
+ * transformer (arXiv 2607.28144; index page, "Abstract") whose blocks attend
+ * over the video-latent token sequence of one decode window, split into
+ * attention heads (blog summary, "Methodology - deep read", the USP
+ * paragraph: Ulysses reshuffles the sequence into heads). The pages require
+ * the attention to stay exact (blog summary, "Technical innovations", USP
+ * bullet) and cite FlashAttention / FlashAttention-2 (index page, "Builds
+ * on"). For every head and query token m this library computes
+ *
+ *     o_m = sum_n softmax_n( sm_scale * <R(m) q_m, R(n) k_n> ) v_n
+ *
+ * over all tokens n of the window (non-causal), where R(n) is a rotary
+ * position embedding over the token's (t, h, w) latent coordinates. The
+ * pages give no rotary convention; this library fixes it as follows:
+ *   - token n of the T x H x W grid sits at t = n / (H W), h = (n / W) % H,
+ *     w = n % W (row-major, t slowest), with origin 0 on every axis;
+ *   - the head_dim/2 pairs (x[2i], x[2i+1]) are split into consecutive
+ *     chunks of pairs_t, pairs_h, pairs_w pairs for the t, h, w axes;
+ *   - pair j of axis a turns counter-clockwise by pos_a * base^(-j/P_a).
+ *
+ * Numerics: inputs and output are bf16; rotated Q and K are rounded to bf16,
+ * both products use bf16 MFMA with fp32 accumulation, the softmax runs in
+ * fp32 (exp2 with the scale folded in), probabilities are rounded to bf16
+ * for the P V product, and the output is rounded to bf16
+ * (round-to-nearest-even throughout).
+ *
+ * Layout: q, k, v, o are contiguous bf16 tensors [heads][T*H*W][head_dim]
+ * in device memory, 16-byte aligned, owned by the caller.
+ *
+ * Threading: a handle is bound to the HIP device that was current at
+ * create. It owns a device workspace (rotated K and a transposed V), so calls
+ * of regen_attn_forward on ONE handle must be ordered: issue them on one
+ * stream, or synchronize between streams. Distinct handles are independent.
+ */
+#ifndef REGEN_ATTN_H
+#define REGEN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum regen_status {
+    REGEN_OK = 0,
+    REGEN_ERR_INVALID_ARGUMENT = 1, /* a NULL, out-of-range or misaligned argument */
+    REGEN_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head_dim, device) */
+    REGEN_ERR_NO_DEVICE = 3,        /* no usable HIP device */
+    REGEN_ERR_OUT_OF_MEMORY = 4,    /* device or host allocation failed */
+    REGEN_ERR_HIP = 5               /* a HIP runtime call failed; see regen_attn_last_error */
+} regen_status;
+
+/* Flags for regen_attn_desc.flags. */
+#define REGEN_ATTN_NO_ROPE 0x1u /* skip the rotation (plain exact attention) */
+#define REGEN_ATTN_PROFILE 0x2u /* record HIP events around each kernel (see
+                                   regen_attn_profile_read) */
+
+/*
+ * Problem description. Zero in an optional field selects its default.
+ *   struct_size : sizeof(regen_attn_desc) (version check)
+ *   heads       : attention heads, >= 1
+ *   head_dim    : 64 or 128
+ *   grid_t/h/w  : latent grid; tokens = grid_t * grid_h * grid_w, >= 1
+ *   pairs_t/h/w : rotary pairs per axis; all three 0 selects the default
+ *                 split (h and w get floor(head_dim/6) each, t the rest:
+ *                 22/21/21 at head_dim 128, 12/10/10 at 64); otherwise each
+ *                 must be >= 1 and they must sum to head_dim / 2
+ *   rope_base   : rotary base, > 0 (0 selects 10000)
+ *   sm_scale    : softmax scale, > 0 (0 selects 1/sqrt(head_dim))
+ *   flags       : REGEN_ATTN_* bits
+ */
+typedef struct regen_attn_desc {
+    uint32_t struct_size;
+    int32_t heads;
+    int32_t head_dim;
+    int32_t grid_t;
+    int32_t grid_h;
+    int32_t grid_w;
+    int32_t pairs_t;
+    int32_t pairs_h;
+    int32_t pairs_w;
+    float rope_base;
+    float sm_scale;
+    uint32_t flags;
+} regen_attn_desc;
+
+typedef struct regen_attn *regen_attn_t;
+
+/*
+ * Create a handle for one problem shape on the current HIP device.
+ * Allocates the handle, the per-axis rotary tables (fp64 on the host,
+ * stored as fp32 cos/sin) and a device workspace of
+ * 2 * heads * ceil(tokens/128)*128 * head_dim * 2 bytes.
+ * On success *out receives the handle; on any failure *out is set to NULL
+ * (when out is not NULL) and the status says why:
+ *   INVALID_ARGUMENT (NULL desc/out, wrong struct_size, heads/grid < 1,
+ *   bad pairs split, base or scale < 0, unknown flags, tokens > 2^30),
+ *   UNSUPPORTED (head_dim not 64/128, current device is not gfx950),
+ *   NO_DEVICE, OUT_OF_MEMORY, HIP.
+ */
+regen_status regen_attn_create(const regen_attn_desc *desc, regen_attn_t *out);
+
+/*
+ * Enqueue one attention call on `stream` (a hipStream_t; NULL = the null
+ * stream) and return without waiting. q, k, v (inputs) and o (output) are
+ * device pointers to contiguous bf16 [heads][tokens][head_dim] tensors,
+ * 16-byte aligned; o must not overlap q, k or v. The buffer sizes cannot be
+ * checked from raw pointers: each must hold heads * tokens * head_dim bf16
+ * values. Errors: INVALID_ARGUMENT (NULL or destroyed handle, NULL or
+ * misaligned pointer, o overlapping an input), HIP (launch failure; detail
+ * in regen_attn_last_error). Faults during execution surface at the
+ * caller's next synchronization.
+ */
+regen_status regen_attn_forward(regen_attn_t h, const void *q, const void *k,
+                                const void *v, void *o, void *stream);
+
+/*
+ * Free the handle, its tables and workspace. No call on the handle may still
+ * be in flight (the device memory is released immediately). NULL is a no-op
+ * returning REGEN_OK; a handle that is not live gives INVALID_ARGUMENT.
+ */
+regen_status regen_attn_destroy(regen_attn_t h);
+
+/* Static, human-readable name of a status code. Never NULL; do not free. */
+const char *regen_attn_status_string(regen_status s);
+
+/*
+ * Detail of the last failure on the calling thread (thread-local storage;
+ * empty string if none). Valid until the next library call on this thread.
+ */
+const char *regen_attn_last_error(void);
+
+/*
+ * Kernel timing for handles created with REGEN_ATTN_PROFILE. Each forward
+ * then records HIP events on its stream before and after each of its two
+ * kernels (the K-rotation / V-transpose pass and the attention kernel).
+ * This call waits for the events of every forward issued since the last
+ * read, adds their durations (milliseconds) to *prep_ms and *attn_ms and the
+ * number of forwards to *calls (each output may be NULL), and forgets them.
+ * Errors: INVALID_ARGUMENT (handle not live, or created without the flag),
+ * HIP (event failure).
+ */
+regen_status regen_attn_profile_read(regen_attn_t h, double *prep_ms, double *attn_ms,
+                                     int64_t *calls);
+
+/*
+ * Workspace bytes regen_attn_create would allocate for desc, or 0 if the
+ * description is invalid. Touches no device.
+ */
+size_t regen_attn_workspace_size(const regen_attn_desc *desc);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REGEN_ATTN_H */
