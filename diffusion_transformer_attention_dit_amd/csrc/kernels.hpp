@@ -161,6 +161,55 @@ __device__ __forceinline__ int xcd_remap(int b, int G) {
     return (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
 }
 
+// Byte offset of 16-byte chunk c of row r in an LDS tile whose rows are RB
+// bytes (128 or 256) and stored unpadded. Chunks are XOR-swizzled by row so
+// that the MFMA operand reads (32 rows, one chunk column) are free of bank
+// conflicts; the swizzle is its own inverse.
+template <int RB>
+__device__ __forceinline__ int swz_off(int r, int c) {
+    static_assert(RB == 128 || RB == 256, "row bytes");
+    const int pc = (RB == 256) ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+    return r * RB + pc * 16;
+}
+
+// One wave-wide 16-byte-per-lane copy global -> LDS without registers
+// (global_load_lds_dwordx4): lane i's 16 bytes land at lds_wave_base + 16 i.
+__device__ __forceinline__ void g2lds16(const void* gptr, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gptr,
+                                     (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0,
+                                     0);
+}
+
+// Issue the copies of K tile j (BN rows of Kr) and its Vt slots into LDS
+// buffer (ks, vs). Every wave copies whole 1 KiB runs of the swizzled
+// tiles; lane l of a run at tile position p fetches the logical chunk that
+// the swizzle places at p.
+template <int D, int BN, int NW>
+__device__ __forceinline__ void issue_tile(const char* __restrict__ kbase,
+                                           const char* __restrict__ vbase, int j, char* ks,
+                                           char* vs, int wave, int lane) {
+    constexpr int KRB = D * 2, VRB = BN * 2;  // LDS row bytes
+    constexpr int RUNS = BN * D * 2 / 1024;   // 1 KiB runs per tile (same for K and V)
+    static_assert(RUNS % NW == 0, "runs per wave");
+#pragma unroll
+    for (int i = 0; i < RUNS / NW; ++i) {
+        const int run = i * NW + wave;
+        const int p = run * 64 + lane;  // chunk position in the tile
+        {
+            const int r = p / (KRB / 16), pc = p % (KRB / 16);
+            const int c = (KRB == 256) ? (pc ^ (r & 15)) : (pc ^ ((r >> 1) & 7));
+            g2lds16(kbase + ((size_t)(j * BN + r) * D) * 2 + c * 16, ks + run * 1024);
+        }
+        {
+            const int d = p / (VRB / 16), pc = p % (VRB / 16);
+            const int c = (VRB == 256) ? (pc ^ (d & 15)) : (pc ^ ((d >> 1) & 7));
+            const int blk = c / 8, g = c % 8;
+            g2lds16(vbase + ((size_t)((j * BN / kVtBlk + blk) * D + d) * kVtBlk + g * 8) * 2,
+                    vs + run * 1024);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel 2: attention. Grid heads * ceil(N / (32 NW)), NW * 64 threads.
 // ---------------------------------------------------------------------------
@@ -171,16 +220,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     RopeGeom geo, int N, int Npad, int n_qtiles, float c2 /* sm_scale * log2(e) */) {
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(BN == 64 || BN == 128, "key tile");
-    constexpr int T = NW * 64;
-    constexpr int KSTR = D * 2 + 16;   // LDS bytes per K row (16 B pad: conflict-free b128 reads)
-    constexpr int VSTR = BN * 2 + 16;  // LDS bytes per Vt row
-    constexpr int KBYTES = BN * KSTR, VBYTES = D * VSTR;
-    constexpr int KCH = BN * D / 8, VCH = D * BN / 8;  // 16-byte chunks per tile
-    constexpr int KPT = KCH / T, VPT = VCH / T;
-    static_assert(KCH % T == 0 && VCH % T == 0, "tile/threads");
+    constexpr int KRB = D * 2, VRB = BN * 2;  // LDS row bytes of the K and Vt tiles
+    constexpr int KBYTES = BN * KRB, VBYTES = D * VRB;
     constexpr float kLazy = 8.0f;  // rescale only when the max grows by > 2^8
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * (KBYTES + VBYTES)];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * (KBYTES + VBYTES)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -189,6 +233,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int hd = L / n_qtiles, qt = L % n_qtiles;
     const int qrow = qt * (NW * 32) + wave * 32 + col;
+
+    const int nt = (N + BN - 1) / BN;
+    const char* kbase = reinterpret_cast<const char*>(kr + (size_t)hd * Npad * D);
+    const char* vbase = reinterpret_cast<const char*>(vt + (size_t)hd * Npad * D);
+
+    // Start streaming tile 0 before the Q work.
+    issue_tile<D, BN, NW>(kbase, vbase, 0, smem, smem + KBYTES, wave, lane);
 
     // ---- Q: load this lane's half-rows and rotate them (RoPE on load) ----
     bf16x8 qf[D / 16];
@@ -216,54 +267,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     float m_run = -INFINITY;  // running max in the exp2 domain (scaled)
     float l_run = 0.0f;       // this lane's partial row sum
 
-    const int nt = (N + BN - 1) / BN;
-    const char* kbase = reinterpret_cast<const char*>(kr + (size_t)hd * Npad * D);
-    const char* vbase = reinterpret_cast<const char*>(vt + (size_t)hd * Npad * D);
-
-    uint4 kreg[KPT], vreg[VPT];
-    auto gload = [&](int j) {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int cid = tid + i * T;
-            const int r = cid / (D / 8), c = cid % (D / 8);
-            kreg[i] = *reinterpret_cast<const uint4*>(kbase + ((size_t)(j * BN + r) * D + c * 8) * 2);
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int cid = tid + i * T;
-            const int blk = cid / (D * 8), rem = cid % (D * 8);
-            const int d = rem / 8, g = rem % 8;
-            vreg[i] = *reinterpret_cast<const uint4*>(
-                vbase + ((size_t)((j * BN / kVtBlk + blk) * D + d) * kVtBlk + g * 8) * 2);
-        }
-    };
-    auto lstore = [&](int buf) {
-        char* ks = smem + buf * (KBYTES + VBYTES);
-        char* vs = ks + KBYTES;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int cid = tid + i * T;
-            const int r = cid / (D / 8), c = cid % (D / 8);
-            *reinterpret_cast<uint4*>(ks + r * KSTR + c * 16) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int cid = tid + i * T;
-            const int blk = cid / (D * 8), rem = cid % (D * 8);
-            const int d = rem / 8, g = rem % 8;
-            *reinterpret_cast<uint4*>(vs + d * VSTR + (blk * kVtBlk + g * 8) * 2) = vreg[i];
-        }
-    };
-
-    gload(0);
-    lstore(0);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     for (int j = 0; j < nt; ++j) {
         const int buf = j & 1;
-        if (j + 1 < nt) gload(j + 1);
         const char* ks = smem + buf * (KBYTES + VBYTES);
         const char* vs = ks + KBYTES;
+        if (j + 1 < nt) {
+            char* nks = smem + (buf ^ 1) * (KBYTES + VBYTES);
+            issue_tile<D, BN, NW>(kbase, vbase, j + 1, nks, nks + KBYTES, wave, lane);
+        }
 
         // S^T = K Q^T for this tile: BN keys x 32 queries.
         f32x16 s[BN / 32];
@@ -274,7 +288,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int kb = 0; kb < D / 16; ++kb) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    ks + (kk * 32 + col) * KSTR + (kb * 16 + half * 8) * 2);
+                    ks + swz_off<KRB>(kk * 32 + col, kb * 2 + half));
                 s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s[kk], 0, 0, 0);
             }
         }
@@ -337,11 +351,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int kq = 0; kq < BN / 16; ++kq) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    vs + (db * 32 + col) * VSTR + (kq * 16 + half * 8) * 2);
+                    vs + swz_off<VRB>(db * 32 + col, kq * 2 + half));
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kq], acc[db], 0, 0, 0);
             }
 
-        if (j + 1 < nt) lstore(buf ^ 1);
+        // The next tile's copies must have landed (this wave's: vmcnt; the
+        // others': the barrier) before anyone reads them, and every wave must
+        // be done with this buffer before it is refilled.
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
