@@ -31,7 +31,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run 3 device-to-device copies of this many MiB (to scale HBM "
+                         "byte counters against a copy of known size) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n * 4,
+                                           "bytes_written_per_copy": n * 4, "copies": 3}}))
+    return 0
 
 
 def cpu_baseline(w, target_s):
@@ -98,6 +114,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration_mib:
+        return copy_calibration(args.copy_calibration_mib)
     native.lib()  # fail loudly if the HIP library is missing
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)

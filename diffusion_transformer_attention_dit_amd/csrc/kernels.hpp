@@ -172,12 +172,22 @@ __device__ __forceinline__ int swz_off(int r, int c) {
     return r * RB + pc * 16;
 }
 
+// Buffer resource over `bytes` bytes at `base` (raw, untyped 32-bit data
+// format); accesses past `bytes` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
 // One wave-wide 16-byte-per-lane copy global -> LDS without registers
-// (global_load_lds_dwordx4): lane i's 16 bytes land at lds_wave_base + 16 i.
-__device__ __forceinline__ void g2lds16(const void* gptr, void* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gptr,
-                                     (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0,
-                                     0);
+// (buffer_load_dwordx4 ... lds): lane i's 16 bytes, read at byte `voff` of
+// the resource, land at lds_wave_base + 16 i. The MUBUF form is used rather
+// than the global (FLAT) one so that LDS reads issued while copies are in
+// flight keep precise, in-order wait counts.
+__device__ __forceinline__ void g2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                        void* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                             16, voff, 0, 0, 0);
 }
 
 // Issue the copies of K tile j (BN rows of Kr) and its Vt slots into LDS
@@ -185,9 +195,8 @@ __device__ __forceinline__ void g2lds16(const void* gptr, void* lds_wave_base) {
 // tiles; lane l of a run at tile position p fetches the logical chunk that
 // the swizzle places at p.
 template <int D, int BN, int NW>
-__device__ __forceinline__ void issue_tile(const char* __restrict__ kbase,
-                                           const char* __restrict__ vbase, int j, char* ks,
-                                           char* vs, int wave, int lane) {
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                           int j, char* ks, char* vs, int wave, int lane) {
     constexpr int KRB = D * 2, VRB = BN * 2;  // LDS row bytes
     constexpr int RUNS = BN * D * 2 / 1024;   // 1 KiB runs per tile (same for K and V)
     static_assert(RUNS % NW == 0, "runs per wave");
@@ -198,13 +207,13 @@ __device__ __forceinline__ void issue_tile(const char* __restrict__ kbase,
         {
             const int r = p / (KRB / 16), pc = p % (KRB / 16);
             const int c = (KRB == 256) ? (pc ^ (r & 15)) : (pc ^ ((r >> 1) & 7));
-            g2lds16(kbase + ((size_t)(j * BN + r) * D) * 2 + c * 16, ks + run * 1024);
+            g2lds16(krs, (uint32_t)((j * BN + r) * D * 2 + c * 16), ks + run * 1024);
         }
         {
             const int d = p / (VRB / 16), pc = p % (VRB / 16);
             const int c = (VRB == 256) ? (pc ^ (d & 15)) : (pc ^ ((d >> 1) & 7));
             const int blk = c / 8, g = c % 8;
-            g2lds16(vbase + ((size_t)((j * BN / kVtBlk + blk) * D + d) * kVtBlk + g * 8) * 2,
+            g2lds16(vrs, (uint32_t)((((j * BN / kVtBlk + blk) * D + d) * kVtBlk + g * 8) * 2),
                     vs + run * 1024);
         }
     }
@@ -235,11 +244,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int qrow = qt * (NW * 32) + wave * 32 + col;
 
     const int nt = (N + BN - 1) / BN;
-    const char* kbase = reinterpret_cast<const char*>(kr + (size_t)hd * Npad * D);
-    const char* vbase = reinterpret_cast<const char*>(vt + (size_t)hd * Npad * D);
+    // This head's Kr rows and Vt blocks (Npad * D bf16 each).
+    const uint32_t head_bytes = (uint32_t)Npad * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kr + (size_t)hd * Npad * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt + (size_t)hd * Npad * D, head_bytes);
 
     // Start streaming tile 0 before the Q work.
-    issue_tile<D, BN, NW>(kbase, vbase, 0, smem, smem + KBYTES, wave, lane);
+    issue_tile<D, BN, NW>(krs, vrs, 0, smem, smem + KBYTES, wave, lane);
 
     // ---- Q: load this lane's half-rows and rotate them (RoPE on load) ----
     bf16x8 qf[D / 16];
@@ -276,21 +287,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const char* vs = ks + KBYTES;
         if (j + 1 < nt) {
             char* nks = smem + (buf ^ 1) * (KBYTES + VBYTES);
-            issue_tile<D, BN, NW>(kbase, vbase, j + 1, nks, nks + KBYTES, wave, lane);
+            issue_tile<D, BN, NW>(krs, vrs, j + 1, nks, nks + KBYTES, wave, lane);
         }
+
+        // MFMA A operands come from LDS through a ring of RING fragments read
+        // ahead of their use: fragments 0..NK-1 are the K tile (key block kk,
+        // head-dim block kb), NK..NK+NV-1 the Vt tile (head-dim block db,
+        // key block kq). The first Vt fragments are requested during the S
+        // products, before the softmax needs the MFMA results.
+        constexpr int KB = D / 16, NK = (BN / 32) * KB, QB16 = BN / 16, NV = (D / 32) * QB16;
+        constexpr int RING = 8;
+        auto frag = [&](int f) -> bf16x8 {
+            if (f < NK) {
+                const int kk = f / KB, kb = f % KB;
+                return *reinterpret_cast<const bf16x8*>(ks + swz_off<KRB>(kk * 32 + col, kb * 2 + half));
+            }
+            const int g = f - NK, db = g / QB16, kq = g % QB16;
+            return *reinterpret_cast<const bf16x8*>(vs + swz_off<VRB>(db * 32 + col, kq * 2 + half));
+        };
+        bf16x8 fr[RING];
+#pragma unroll
+        for (int f = 0; f < RING; ++f) fr[f] = frag(f);
 
         // S^T = K Q^T for this tile: BN keys x 32 queries.
         f32x16 s[BN / 32];
 #pragma unroll
-        for (int kk = 0; kk < BN / 32; ++kk) {
+        for (int f = 0; f < NK; ++f) {
+            const int kk = f / KB, kb = f % KB;
+            if (kb == 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[kk][i] = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < D / 16; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    ks + swz_off<KRB>(kk * 32 + col, kb * 2 + half));
-                s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s[kk], 0, 0, 0);
+                for (int i = 0; i < 16; ++i) s[kk][i] = 0.0f;
             }
+            s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % RING], qf[kb], s[kk], 0, 0, 0);
+            if (f + RING < NK + NV) fr[f % RING] = frag(f + RING);
         }
 
         // Keys past the end of the sequence get -inf (never zero-padding).
@@ -347,13 +376,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
         // O^T += V^T P^T.
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int kq = 0; kq < BN / 16; ++kq) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    vs + swz_off<VRB>(db * 32 + col, kq * 2 + half));
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kq], acc[db], 0, 0, 0);
-            }
+        for (int g = 0; g < NV; ++g) {
+            const int f = NK + g, db = g / QB16, kq = g % QB16;
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % RING], p[kq], acc[db], 0, 0, 0);
+            if (f + RING < NK + NV) fr[f % RING] = frag(f + RING);
+        }
 
         // The next tile's copies must have landed (this wave's: vmcnt; the
         // others': the barrier) before anyone reads them, and every wave must
