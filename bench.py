@@ -153,10 +153,11 @@ def main():
     for _ in range(max(1, args.steps // 2)):
         for (q, k, v), i in zip(drv.inputs, range(len(drv.inputs))):
             prof.forward(q, k, v, out=drv.outs[i & 1], stream=stream)
-    prep_ms, attn_ms, n_calls = prof.profile_read()
+    prep_ms, attn_ms, merge_ms, n_calls = prof.profile_read()
     prof.close()
     attn_avg_s = attn_ms / n_calls * 1e-3
     prep_avg_s = prep_ms / n_calls * 1e-3
+    merge_avg_s = merge_ms / n_calls * 1e-3
     attn_tflops = w.flops_per_call / attn_avg_s / 1e12
     prep_bytes = 4 * w.heads * w.tokens * w.head_dim * 2  # read K, V; write Kr, Vt
 
@@ -199,6 +200,7 @@ def main():
             "achieved": round(prep_bytes / prep_avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(prep_bytes / prep_avg_s / 1e9 / PEAK_HBM_GBS, 4),
         },
+        "merge_kernel": {"kernel": "merge_kernel", "avg_launch_us": round(merge_avg_s * 1e6, 2)},
     }
     drv.close()
     del drv

@@ -77,9 +77,11 @@ __device__ __forceinline__ float2 rope_cs(const float2* __restrict__ tab, const 
     return tab[idx];
 }
 
-// Rotate the 4 pairs held in one 16-byte chunk (8 bf16, pairs i0..i0+3).
+// Rotate the 4 pairs held in one 16-byte chunk (8 bf16, pairs i0..i0+3),
+// scale by `mul` and round to bf16.
 __device__ __forceinline__ uint4 rope_chunk(uint4 in, const float2* __restrict__ tab,
-                                            const RopeGeom& g, int i0, int t, int h, int w) {
+                                            const RopeGeom& g, int i0, int t, int h, int w,
+                                            float mul = 1.0f) {
     uint32_t src[4] = {in.x, in.y, in.z, in.w};
     uint32_t dst[4];
 #pragma unroll
@@ -88,7 +90,7 @@ __device__ __forceinline__ uint4 rope_chunk(uint4 in, const float2* __restrict__
         float x = bf_lo(src[p]), y = bf_hi(src[p]);
         float xr = x * cs.x - y * cs.y;
         float yr = x * cs.y + y * cs.x;
-        dst[p] = pack_bf16(xr, yr);
+        dst[p] = pack_bf16(xr * mul, yr * mul);
     }
     return make_uint4(dst[0], dst[1], dst[2], dst[3]);
 }
@@ -220,15 +222,49 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: attention. Grid heads * ceil(N / (32 NW)), NW * 64 threads.
+// Work schedule (stream-K style). A "unit" is one (query tile, key block)
+// pair: query tile t (BM = 32 NW rows of one head) against key block b (BN
+// keys); unit index x = t * nkv + b, tiles numbered head-major. The P
+// persistent workgroups take equal contiguous unit ranges, so every
+// resident slot of the GPU gets the same work whatever the tile count. A
+// tile whose units span several workgroups is finished by the merge kernel
+// from the per-workgroup partial results (unnormalised O, running max m,
+// row sum l), combined exactly as in blockwise softmax.
+// ---------------------------------------------------------------------------
+struct Sched {
+    int n_qtiles;     // query tiles per head
+    int nkv;          // key blocks per tile
+    long long units;  // heads * n_qtiles * nkv
+    int P;            // persistent workgroups (1 <= P <= units)
+};
+
+__device__ __forceinline__ long long unit_begin(const Sched& sc, int p) {
+    return (long long)p * sc.units / sc.P;
+}
+// The workgroup whose range holds unit x.
+__device__ __forceinline__ int unit_owner(const Sched& sc, long long x) {
+    return (int)(((x + 1) * sc.P - 1) / sc.units);
+}
+// Partial-result slot of workgroup p for tile t: its first tile uses 2p, a
+// later (necessarily last) tile uses 2p + 1.
+__device__ __forceinline__ int partial_slot(const Sched& sc, int p, long long t) {
+    return (t == unit_begin(sc, p) / sc.nkv) ? 2 * p : 2 * p + 1;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: attention, persistent. Grid P, NW * 64 threads.
+//   part_o  : [2P][BM][D] fp32 unnormalised O of split tiles
+//   part_ml : [2P][BM][2] fp32 (m, l) of split tiles
 // ---------------------------------------------------------------------------
 template <int D, int BN, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, const float2* __restrict__ tab,
-    RopeGeom geo, int N, int Npad, int n_qtiles, float c2 /* sm_scale * log2(e) */) {
+    RopeGeom geo, int N, int Npad, Sched sc, float c2 /* sm_scale * log2(e) */,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(BN == 64 || BN == 128, "key tile");
+    constexpr int BM = NW * 32;
     constexpr int KRB = D * 2, VRB = BN * 2;  // LDS row bytes of the K and Vt tiles
     constexpr int KBYTES = BN * KRB, VBYTES = D * VRB;
     constexpr float kLazy = 8.0f;  // rescale only when the max grows by > 2^8
@@ -239,175 +275,296 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, half = lane >> 5;
 
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int hd = L / n_qtiles, qt = L % n_qtiles;
-    const int qrow = qt * (NW * 32) + wave * 32 + col;
+    // Consecutive logical workgroups (hence consecutive tiles of one head)
+    // share an XCD and its L2.
+    const int pid = xcd_remap(blockIdx.x, gridDim.x);
+    const long long u0 = unit_begin(sc, pid), u1 = unit_begin(sc, pid + 1);
+    if (u0 >= u1) return;  // uniform over the block; no barrier reached yet
+    const long long first_tile = u0 / sc.nkv;
 
-    const int nt = (N + BN - 1) / BN;
-    // This head's Kr rows and Vt blocks (Npad * D bf16 each).
     const uint32_t head_bytes = (uint32_t)Npad * D * 2;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kr + (size_t)hd * Npad * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt + (size_t)hd * Npad * D, head_bytes);
+    const int HW = geo.H * geo.W;
 
-    // Start streaming tile 0 before the Q work.
-    issue_tile<D, BN, NW>(krs, vrs, 0, smem, smem + KBYTES, wave, lane);
+    // Copy the K/V block of unit (tile t, block b) into LDS buffer `buf`.
+    auto issue_unit = [&](long long t, int b, int buf) {
+        const int h = (int)(t / sc.n_qtiles);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kr + (size_t)h * Npad * D, head_bytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt + (size_t)h * Npad * D, head_bytes);
+        char* ks = smem + buf * (KBYTES + VBYTES);
+        issue_tile<D, BN, NW>(krs, vrs, b, ks, ks + KBYTES, wave, lane);
+    };
 
-    // ---- Q: load this lane's half-rows and rotate them (RoPE on load) ----
-    bf16x8 qf[D / 16];
-    {
-        const int HW = geo.H * geo.W;
-        const int qn = qrow < N ? qrow : 0;
-        const int t = qn / HW, h = (qn / geo.W) % geo.H, w = qn % geo.W;
-        const uint16_t* qp = q + ((size_t)hd * N + qn) * D + half * 8;
+    issue_unit(first_tile, (int)(u0 - first_tile * sc.nkv), 0);
+    int buf = 0;
+    long long u = u0;
+
+    while (u < u1) {
+        // ---- one segment: tile t, key blocks [kv0, kv1) ----
+        const long long t = u / sc.nkv;
+        const int kv0 = (int)(u - t * sc.nkv);
+        const long long seg_end = ((t + 1) * sc.nkv < u1) ? (t + 1) * sc.nkv : u1;
+        const int kv1 = kv0 + (int)(seg_end - u);
+        const int hd = (int)(t / sc.n_qtiles), qt = (int)(t % sc.n_qtiles);
+        const int qrow = qt * BM + wave * 32 + col;
+
+        // Q: load this lane's half-rows, rotate them (RoPE on load) and fold
+        // in the softmax scale and log2(e), so that Q K^T comes out in the
+        // exp2 domain.
+        bf16x8 qf[D / 16];
+        {
+            const int qn = qrow < N ? qrow : 0;
+            const int tt = qn / HW, hh = (qn / geo.W) % geo.H, ww = qn % geo.W;
+            const uint16_t* qp = q + ((size_t)hd * N + qn) * D + half * 8;
 #pragma unroll
-        for (int kb = 0; kb < D / 16; ++kb) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (qrow < N) {
-                x = *reinterpret_cast<const uint4*>(qp + kb * 16);
-                x = rope_chunk(x, tab, geo, kb * 8 + half * 4, t, h, w);
+            for (int kb = 0; kb < D / 16; ++kb) {
+                uint4 x = make_uint4(0, 0, 0, 0);
+                if (qrow < N) {
+                    x = *reinterpret_cast<const uint4*>(qp + kb * 16);
+                    x = rope_chunk(x, tab, geo, kb * 8 + half * 4, tt, hh, ww, c2);
+                }
+                qf[kb] = __builtin_bit_cast(bf16x8, x);
             }
-            qf[kb] = __builtin_bit_cast(bf16x8, x);
-        }
-    }
-
-    f32x16 acc[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
-    float m_run = -INFINITY;  // running max in the exp2 domain (scaled)
-    float l_run = 0.0f;       // this lane's partial row sum
-
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    for (int j = 0; j < nt; ++j) {
-        const int buf = j & 1;
-        const char* ks = smem + buf * (KBYTES + VBYTES);
-        const char* vs = ks + KBYTES;
-        if (j + 1 < nt) {
-            char* nks = smem + (buf ^ 1) * (KBYTES + VBYTES);
-            issue_tile<D, BN, NW>(krs, vrs, j + 1, nks, nks + KBYTES, wave, lane);
         }
 
-        // MFMA A operands come from LDS through a ring of RING fragments read
-        // ahead of their use: fragments 0..NK-1 are the K tile (key block kk,
-        // head-dim block kb), NK..NK+NV-1 the Vt tile (head-dim block db,
-        // key block kq). The first Vt fragments are requested during the S
-        // products, before the softmax needs the MFMA results.
-        constexpr int KB = D / 16, NK = (BN / 32) * KB, QB16 = BN / 16, NV = (D / 32) * QB16;
-        constexpr int RING = 8;
-        auto frag = [&](int f) -> bf16x8 {
-            if (f < NK) {
+        f32x16 acc[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
+        // Running reference value of the row max (exp2 domain); -m_run fills
+        // every slot of negm, the accumulator input of each key block's first
+        // S MFMA, so the products come out already shifted: s = S - m_run.
+        float m_run = 0.0f;
+        f32x16 negm;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) negm[i] = 0.0f;
+        float l0 = 0.0f, l1 = 0.0f;  // this lane's partial row sums
+
+        if (u == u0) {
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+
+        for (int b = kv0; b < kv1; ++b, ++u) {
+            const char* ks = smem + buf * (KBYTES + VBYTES);
+            const char* vs = ks + KBYTES;
+            if (u + 1 < u1) {
+                const bool same = b + 1 < sc.nkv;
+                issue_unit(same ? t : t + 1, same ? b + 1 : 0, buf ^ 1);
+            }
+
+            // MFMA A operands come from LDS through a ring of RING fragments
+            // read ahead of their use: fragments 0..NK-1 are the K tile (key
+            // block kk, head-dim block kb), NK..NK+NV-1 the Vt tile (head-dim
+            // block db, key block kq). The first Vt fragments are requested
+            // during the S products, before the softmax needs them.
+            constexpr int KB = D / 16, NK = (BN / 32) * KB, QB16 = BN / 16, NV = (D / 32) * QB16;
+            constexpr int RING = 8;
+            auto frag = [&](int f) -> bf16x8 {
+                if (f < NK) {
+                    const int kk = f / KB, kb = f % KB;
+                    return *reinterpret_cast<const bf16x8*>(ks + swz_off<KRB>(kk * 32 + col, kb * 2 + half));
+                }
+                const int g = f - NK, db = g / QB16, kq = g % QB16;
+                return *reinterpret_cast<const bf16x8*>(vs + swz_off<VRB>(db * 32 + col, kq * 2 + half));
+            };
+            bf16x8 fr[RING];
+#pragma unroll
+            for (int f = 0; f < RING; ++f) fr[f] = frag(f);
+
+            // S^T = K Q^T - m_run for this block: BN keys x 32 queries.
+            f32x16 s[BN / 32];
+#pragma unroll
+            for (int f = 0; f < NK; ++f) {
                 const int kk = f / KB, kb = f % KB;
-                return *reinterpret_cast<const bf16x8*>(ks + swz_off<KRB>(kk * 32 + col, kb * 2 + half));
+                s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % RING], qf[kb],
+                                                                kb == 0 ? negm : s[kk], 0, 0, 0);
+                if (f + RING < NK + NV) fr[f % RING] = frag(f + RING);
             }
-            const int g = f - NK, db = g / QB16, kq = g % QB16;
-            return *reinterpret_cast<const bf16x8*>(vs + swz_off<VRB>(db * 32 + col, kq * 2 + half));
-        };
-        bf16x8 fr[RING];
-#pragma unroll
-        for (int f = 0; f < RING; ++f) fr[f] = frag(f);
 
-        // S^T = K Q^T for this tile: BN keys x 32 queries.
-        f32x16 s[BN / 32];
+            // Keys past the end of the sequence get -inf (never zero-padding).
+            if (b == sc.nkv - 1 && (N % BN) != 0) {
 #pragma unroll
-        for (int f = 0; f < NK; ++f) {
-            const int kk = f / KB, kb = f % KB;
-            if (kb == 0) {
+                for (int kk = 0; kk < BN / 32; ++kk)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[kk][i] = 0.0f;
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = b * BN + kk * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+                        if (key >= N) s[kk][i] = -INFINITY;
+                    }
             }
-            s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % RING], qf[kb], s[kk], 0, 0, 0);
-            if (f + RING < NK + NV) fr[f % RING] = frag(f + RING);
-        }
 
-        // Keys past the end of the sequence get -inf (never zero-padding).
-        if (j == nt - 1 && (N % BN) != 0) {
+            // Row max of s: in-lane over this lane's keys (4 independent
+            // chains), then with lane ^ 32, which holds the row's other keys.
+            float mp[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
             for (int kk = 0; kk < BN / 32; ++kk)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = j * BN + kk * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-                    if (key >= N) s[kk][i] = -INFINITY;
+                for (int i = (kk == 0 ? 4 : 0); i < 16; ++i) mp[i & 3] = fmaxf(mp[i & 3], s[kk][i]);
+            float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+            {
+                auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                           false, false);
+                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            // Lazy rescale: keep the reference m_run unless the row max passes
+            // it by more than kLazy, so P = exp2(s) stays <= 2^kLazy; the final
+            // O / l is exact for any such reference. The segment's first block
+            // always sets it.
+            const bool first = (b == kv0);
+            if (first || mx > kLazy) {
+                if (!first) {
+                    const float alpha = __builtin_amdgcn_exp2f(-mx);
+                    l0 *= alpha;
+                    l1 *= alpha;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
                 }
-        }
-
-        // Row max: in-lane over this lane's keys, then with lane ^ 32.
-        float mx = s[0][0];
+                m_run += mx;
 #pragma unroll
-        for (int kk = 0; kk < BN / 32; ++kk)
+                for (int kk = 0; kk < BN / 32; ++kk)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kk][i]);
-        {
-            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                       false, false);
-            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float m_new = mx * c2;
-        // Lazy rescale: the final O / l is exact for any reference value m_run
-        // not below the true max by more than kLazy (P stays <= 2^kLazy).
-        if (m_new > m_run + kLazy) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
+                    for (int i = 0; i < 16; ++i) s[kk][i] -= mx;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-        }
-
-        // P = exp2(S * c2 - m_run), bf16 for the second product.
-        bf16x8 p[BN / 16];
-#pragma unroll
-        for (int kk = 0; kk < BN / 32; ++kk)
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                uint32_t w4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kk][hb * 8 + 2 * e], c2, -m_run));
-                    const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kk][hb * 8 + 2 * e + 1], c2, -m_run));
-                    l_run += e0 + e1;
-                    w4[e] = pack_bf16(e0, e1);
-                }
-                p[kk * 2 + hb] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+                for (int i = 0; i < 16; ++i) negm[i] = -m_run;
             }
 
-        // O^T += V^T P^T.
+            // P = exp2(s), rounded to bf16 for the second product; the row sum
+            // accumulates the rounded values (v_dot2 with ones).
+            bf16x8 pk[BN / 16];
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-        for (int g = 0; g < NV; ++g) {
-            const int f = NK + g, db = g / QB16, kq = g % QB16;
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % RING], p[kq], acc[db], 0, 0, 0);
-            if (f + RING < NK + NV) fr[f % RING] = frag(f + RING);
+            for (int kk = 0; kk < BN / 32; ++kk)
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    uint32_t w4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float e0 = __builtin_amdgcn_exp2f(s[kk][hb * 8 + 2 * e]);
+                        const float e1 = __builtin_amdgcn_exp2f(s[kk][hb * 8 + 2 * e + 1]);
+                        w4[e] = pack_bf16(e0, e1);
+                        if (e & 1)
+                            l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[e]), ones, l1, false);
+                        else
+                            l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[e]), ones, l0, false);
+                    }
+                    pk[kk * 2 + hb] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+                }
+
+            // O^T += V^T P^T.
+#pragma unroll
+            for (int g = 0; g < NV; ++g) {
+                const int f = NK + g, db = g / QB16, kq = g % QB16;
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % RING], pk[kq], acc[db], 0, 0, 0);
+                if (f + RING < NK + NV) fr[f % RING] = frag(f + RING);
+            }
+
+            // The next block's copies must have landed (this wave's: vmcnt;
+            // the others': the barrier) before anyone reads them, and every
+            // wave must be done with this buffer before it is refilled.
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            buf ^= 1;
         }
 
-        // The next tile's copies must have landed (this wave's: vmcnt; the
-        // others': the barrier) before anyone reads them, and every wave must
-        // be done with this buffer before it is refilled.
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
-
-    // ---- epilogue: O = O^T / l, bf16 ----
-    {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run),
+        // ---- segment epilogue ----
+        const float l_half = l0 + l1;
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_half), __float_as_uint(l_half),
                                                    false, false);
-        const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const float inv = 1.0f / l_tot;
-        if (qrow < N) {
-            uint16_t* op = o + ((size_t)hd * N + qrow) * D;
+        const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        if (kv0 == 0 && kv1 == sc.nkv) {
+            // Whole tile here: O = O^T / l, bf16.
+            const float inv = 1.0f / l_row;
+            if (qrow < N) {
+                uint16_t* op = o + ((size_t)hd * N + qrow) * D;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int d0 = db * 32 + g4 * 8 + half * 4;
+                        uint2 w2;
+                        w2.x = pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv);
+                        w2.y = pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv);
+                        *reinterpret_cast<uint2*>(op + d0) = w2;
+                    }
+            }
+        } else {
+            // Part of a tile: leave (unnormalised O, m, l) for the merge.
+            const int slot = partial_slot(sc, pid, t);
+            const int r = wave * 32 + col;
+            float* po = part_o + ((size_t)slot * BM + r) * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int d0 = db * 32 + g4 * 8 + half * 4;
-                    uint2 w2;
-                    w2.x = pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv);
-                    w2.y = pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv);
-                    *reinterpret_cast<uint2*>(op + d0) = w2;
+                    *reinterpret_cast<float4*>(po + d0) =
+                        make_float4(acc[db][g4 * 4 + 0], acc[db][g4 * 4 + 1], acc[db][g4 * 4 + 2],
+                                    acc[db][g4 * 4 + 3]);
                 }
+            if (half == 0)
+                *reinterpret_cast<float2*>(part_ml + ((size_t)slot * BM + r) * 2) = make_float2(m_run, l_row);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 3: merge of split tiles. Grid heads * n_qtiles, 256 threads; a tile
+// held whole by one workgroup returns at once. Row r of a split tile:
+//   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o,
+                                                    const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml, int N,
+                                                    Sched sc) {
+    constexpr int BM = NW * 32;
+    constexpr int TPR = 256 / BM;  // threads per row
+    constexpr int DPT = D / TPR;   // head dims per thread
+    static_assert(DPT % 4 == 0, "vector width");
+    const long long t = blockIdx.x;
+    const int p0 = unit_owner(sc, t * sc.nkv);
+    const int p1 = unit_owner(sc, (t + 1) * sc.nkv - 1);
+    if (p0 == p1) return;
+    const int hd = (int)(t / sc.n_qtiles), qt = (int)(t % sc.n_qtiles);
+    const int r = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DPT;
+    const int qrow = qt * BM + r;
+    if (qrow >= N) return;
+    float M = -INFINITY;
+    for (int p = p0; p <= p1; ++p) {
+        const int slot = partial_slot(sc, p, t);
+        M = fmaxf(M, part_ml[((size_t)slot * BM + r) * 2]);
+    }
+    float acc[DPT];
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
+    float L = 0.0f;
+    for (int p = p0; p <= p1; ++p) {
+        const int slot = partial_slot(sc, p, t);
+        const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((size_t)slot * BM + r) * 2);
+        const float w = __builtin_amdgcn_exp2f(ml.x - M);
+        L += w * ml.y;
+        const float* po = part_o + ((size_t)slot * BM + r) * D + d0;
+#pragma unroll
+        for (int i = 0; i < DPT; i += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(po + i);
+            acc[i] += w * x.x;
+            acc[i + 1] += w * x.y;
+            acc[i + 2] += w * x.z;
+            acc[i + 3] += w * x.w;
+        }
+    }
+    const float inv = 1.0f / L;
+    uint16_t* op = o + ((size_t)hd * N + qrow) * D + d0;
+#pragma unroll
+    for (int i = 0; i < DPT; i += 8) {
+        uint4 w4;
+        w4.x = pack_bf16(acc[i] * inv, acc[i + 1] * inv);
+        w4.y = pack_bf16(acc[i + 2] * inv, acc[i + 3] * inv);
+        w4.z = pack_bf16(acc[i + 4] * inv, acc[i + 5] * inv);
+        w4.w = pack_bf16(acc[i + 6] * inv, acc[i + 7] * inv);
+        *reinterpret_cast<uint4*>(op + i) = w4;
     }
 }
 

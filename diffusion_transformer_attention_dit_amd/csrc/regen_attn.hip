@@ -18,6 +18,8 @@
 namespace {
 
 constexpr uint32_t kKnownFlags = REGEN_ATTN_NO_ROPE | REGEN_ATTN_PROFILE;
+// Attention kernel shape: NW waves of 32 query rows, BN-key blocks.
+constexpr int kNW = 4, kBM = kNW * 32, kBN = 64;
 constexpr int64_t kMaxTokens = int64_t(1) << 30;
 
 thread_local std::string g_last_error;
@@ -52,6 +54,8 @@ struct Problem {
     float scale;
     uint32_t flags;
     int64_t tokens, tokens_pad;
+    int n_qtiles, nkv;
+    int64_t units;  // heads * n_qtiles * nkv
 };
 
 regen_status resolve(const regen_attn_desc* d, Problem* p) {
@@ -96,6 +100,9 @@ regen_status resolve(const regen_attn_desc* d, Problem* p) {
     p->flags = d->flags;
     p->tokens = tokens;
     p->tokens_pad = (tokens + regen::kPrepKeys - 1) / regen::kPrepKeys * regen::kPrepKeys;
+    p->n_qtiles = int((tokens + kBM - 1) / kBM);
+    p->nkv = int((tokens + kBN - 1) / kBN);
+    p->units = int64_t(p->heads) * p->n_qtiles * p->nkv;
     return REGEN_OK;
 }
 
@@ -106,10 +113,10 @@ size_t workspace_bytes(const Problem& p) {
 
 }  // namespace
 
-// Events of one profiled forward: before the first kernel, between the two,
-// after the second.
+// Events of one profiled forward: before the first kernel, between
+// consecutive kernels, after the last.
 struct ProfRecord {
-    hipEvent_t ev[3];
+    hipEvent_t ev[4];
 };
 
 struct regen_attn {
@@ -121,7 +128,23 @@ struct regen_attn {
     float2* d_tab;   // rotary (cos, sin) per axis
     uint16_t* d_kr;  // workspace: rotated K
     uint16_t* d_vt;  // workspace: transposed V
+    int P;           // persistent attention workgroups
+    float* d_part_o;   // split-tile partial O   [2P][BM][D]
+    float* d_part_ml;  // split-tile (m, l)       [2P][BM][2]
 };
+
+namespace {
+
+template <int D>
+regen_status occupancy(int* blocks_per_cu) {
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks_per_cu, regen::attn_fwd_kernel<D, kBN, kNW>, kNW * 64, 0);
+    if (e != hipSuccess) return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    if (*blocks_per_cu < 1) *blocks_per_cu = 1;
+    return REGEN_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -202,6 +225,15 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
     h->geo = geo;
     h->d_tab = nullptr;
     h->d_kr = h->d_vt = nullptr;
+    h->d_part_o = h->d_part_ml = nullptr;
+    int per_cu = 1;
+    s = p.head_dim == 128 ? occupancy<128>(&per_cu) : occupancy<64>(&per_cu);
+    if (s != REGEN_OK) {
+        delete h;
+        return s;
+    }
+    const int64_t slots = int64_t(per_cu) * prop.multiProcessorCount;
+    h->P = int(slots < p.units ? slots : p.units);
 
     const size_t tab_bytes = tab.size() * sizeof(float2);
     const size_t half_ws = workspace_bytes(p) / 2;
@@ -209,11 +241,17 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
         if (h->d_tab) (void)hipFree(h->d_tab);
         if (h->d_kr) (void)hipFree(h->d_kr);
         if (h->d_vt) (void)hipFree(h->d_vt);
+        if (h->d_part_o) (void)hipFree(h->d_part_o);
+        if (h->d_part_ml) (void)hipFree(h->d_part_ml);
         delete h;
     };
+    const size_t part_o_bytes = size_t(2) * h->P * kBM * p.head_dim * sizeof(float);
+    const size_t part_ml_bytes = size_t(2) * h->P * kBM * 2 * sizeof(float);
     if ((e = hipMalloc(&h->d_tab, tab_bytes)) != hipSuccess ||
         (e = hipMalloc(&h->d_kr, half_ws)) != hipSuccess ||
-        (e = hipMalloc(&h->d_vt, half_ws)) != hipSuccess) {
+        (e = hipMalloc(&h->d_vt, half_ws)) != hipSuccess ||
+        (e = hipMalloc(&h->d_part_o, part_o_bytes)) != hipSuccess ||
+        (e = hipMalloc(&h->d_part_ml, part_ml_bytes)) != hipSuccess) {
         (void)hipGetLastError();
         cleanup();
         return fail(e == hipErrorOutOfMemory ? REGEN_ERR_OUT_OF_MEMORY : REGEN_ERR_HIP,
@@ -256,9 +294,12 @@ regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, co
     const float c2 = p.scale * 1.4426950408889634f;
 
     dim3 pgrid(unsigned(Npad / regen::kPrepKeys), unsigned(p.heads));
-    constexpr int NW = 4, BN = 64;
-    const int n_qtiles = (N + NW * 32 - 1) / (NW * 32);
-    const unsigned agrid = unsigned(n_qtiles) * unsigned(p.heads);
+    regen::Sched sc;
+    sc.n_qtiles = p.n_qtiles;
+    sc.nkv = p.nkv;
+    sc.units = p.units;
+    sc.P = h->P;
+    const unsigned mgrid = unsigned(p.heads) * unsigned(p.n_qtiles);
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
     const uint16_t* k16 = static_cast<const uint16_t*>(k);
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
@@ -271,7 +312,7 @@ regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, co
             rec = h->prof_free.back();
             h->prof_free.pop_back();
         } else {
-            for (int i = 0; i < 3; ++i) {
+            for (int i = 0; i < 4; ++i) {
                 hipError_t ee = hipEventCreate(&rec.ev[i]);
                 if (ee != hipSuccess) {
                     for (int j = 0; j < i; ++j) (void)hipEventDestroy(rec.ev[j]);
@@ -281,26 +322,34 @@ regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, co
         }
         (void)hipEventRecord(rec.ev[0], st);
     }
-    auto between = [&]() {
-        if (prof) (void)hipEventRecord(rec.ev[1], st);
+    auto mark = [&](int i) {
+        if (prof) (void)hipEventRecord(rec.ev[i], st);
     };
 
     if (p.head_dim == 128) {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<128>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
                            h->d_vt, h->d_tab, h->geo, N, Npad);
-        between();
-        hipLaunchKernelGGL((regen::attn_fwd_kernel<128, BN, NW>), dim3(agrid), dim3(NW * 64), 0, st,
-                           q16, h->d_kr, h->d_vt, o16, h->d_tab, h->geo, N, Npad, n_qtiles, c2);
+        mark(1);
+        hipLaunchKernelGGL((regen::attn_fwd_kernel<128, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
+                           st, q16, h->d_kr, h->d_vt, o16, h->d_tab, h->geo, N, Npad, sc, c2,
+                           h->d_part_o, h->d_part_ml);
+        mark(2);
+        hipLaunchKernelGGL((regen::merge_kernel<128, kNW>), dim3(mgrid), dim3(256), 0, st, o16,
+                           h->d_part_o, h->d_part_ml, N, sc);
     } else {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
                            h->d_vt, h->d_tab, h->geo, N, Npad);
-        between();
-        hipLaunchKernelGGL((regen::attn_fwd_kernel<64, BN, NW>), dim3(agrid), dim3(NW * 64), 0, st,
-                           q16, h->d_kr, h->d_vt, o16, h->d_tab, h->geo, N, Npad, n_qtiles, c2);
+        mark(1);
+        hipLaunchKernelGGL((regen::attn_fwd_kernel<64, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
+                           st, q16, h->d_kr, h->d_vt, o16, h->d_tab, h->geo, N, Npad, sc, c2,
+                           h->d_part_o, h->d_part_ml);
+        mark(2);
+        hipLaunchKernelGGL((regen::merge_kernel<64, kNW>), dim3(mgrid), dim3(256), 0, st, o16,
+                           h->d_part_o, h->d_part_ml, N, sc);
     }
     hipError_t e = hipGetLastError();
     if (prof) {
-        (void)hipEventRecord(rec.ev[2], st);
+        (void)hipEventRecord(rec.ev[3], st);
         h->prof_pending.push_back(rec);
     }
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
@@ -308,28 +357,31 @@ regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, co
 }
 
 regen_status regen_attn_profile_read(regen_attn_t h, double* prep_ms, double* attn_ms,
-                                     int64_t* calls) {
+                                     double* merge_ms, int64_t* calls) {
     g_last_error.clear();
     if (!h || !is_live(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is NULL or not live");
     if (!(h->p.flags & REGEN_ATTN_PROFILE))
         return fail(REGEN_ERR_INVALID_ARGUMENT, "handle was created without REGEN_ATTN_PROFILE");
-    double tp = 0.0, ta = 0.0;
+    double tp = 0.0, ta = 0.0, tm = 0.0;
     int64_t n = 0;
     regen_status st = REGEN_OK;
     for (ProfRecord& r : h->prof_pending) {
-        float a = 0.0f, b = 0.0f;
-        hipError_t e = hipEventSynchronize(r.ev[2]);
+        float a = 0.0f, b = 0.0f, c = 0.0f;
+        hipError_t e = hipEventSynchronize(r.ev[3]);
         if (e == hipSuccess) e = hipEventElapsedTime(&a, r.ev[0], r.ev[1]);
         if (e == hipSuccess) e = hipEventElapsedTime(&b, r.ev[1], r.ev[2]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&c, r.ev[2], r.ev[3]);
         if (e != hipSuccess && st == REGEN_OK) st = fail_hip(e, "profile events");
         tp += a;
         ta += b;
+        tm += c;
         ++n;
         h->prof_free.push_back(r);
     }
     h->prof_pending.clear();
     if (prep_ms) *prep_ms += tp;
     if (attn_ms) *attn_ms += ta;
+    if (merge_ms) *merge_ms += tm;
     if (calls) *calls += n;
     return st;
 }
@@ -347,6 +399,8 @@ regen_status regen_attn_destroy(regen_attn_t h) {
     (void)hipFree(h->d_tab);
     (void)hipFree(h->d_kr);
     (void)hipFree(h->d_vt);
+    (void)hipFree(h->d_part_o);
+    (void)hipFree(h->d_part_ml);
     for (auto* list : {&h->prof_pending, &h->prof_free})
         for (ProfRecord& r : *list)
             for (hipEvent_t ev : r.ev) (void)hipEventDestroy(ev);

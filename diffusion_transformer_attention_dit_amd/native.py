@@ -86,6 +86,7 @@ def lib():
     L.regen_attn_workspace_size.restype = ctypes.c_size_t
     L.regen_attn_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64)]
     L.regen_attn_profile_read.restype = ctypes.c_int
     _LIB = L
@@ -130,10 +131,11 @@ def regen_attn_workspace_size(desc):
 
 
 def regen_attn_profile_read(handle):
-    """Returns (status, prep_ms, attn_ms, calls) accumulated since the last read."""
-    a, b, n = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_int64(0)
-    s = lib().regen_attn_profile_read(handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(n))
-    return s, a.value, b.value, n.value
+    """Returns (status, prep_ms, attn_ms, merge_ms, calls) accumulated since the last read."""
+    a, b, c, n = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0), ctypes.c_int64(0)
+    s = lib().regen_attn_profile_read(handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                      ctypes.byref(n))
+    return s, a.value, b.value, c.value, n.value
 
 
 # ---- a small convenience wrapper over torch tensors ------------------------
@@ -178,11 +180,11 @@ class Attention:
     __call__ = forward
 
     def profile_read(self):
-        """(prep_ms, attn_ms, calls) since the last read; needs REGEN_ATTN_PROFILE."""
-        s, a, b, n = regen_attn_profile_read(self.handle)
+        """(prep_ms, attn_ms, merge_ms, calls) since the last read; needs REGEN_ATTN_PROFILE."""
+        s, a, b, c, n = regen_attn_profile_read(self.handle)
         if s != REGEN_OK:
             raise RegenAttnError(s, "regen_attn_profile_read")
-        return a, b, n
+        return a, b, c, n
 
     def close(self):
         if self.handle is not None:

@@ -94,8 +94,13 @@ typedef struct regen_attn *regen_attn_t;
 /*
  * Create a handle for one problem shape on the current HIP device.
  * Allocates the handle, the per-axis rotary tables (fp64 on the host,
- * stored as fp32 cos/sin) and a device workspace of
- * 2 * heads * ceil(tokens/128)*128 * head_dim * 2 bytes.
+ * stored as fp32 cos/sin), a device workspace of
+ * 2 * heads * ceil(tokens/128)*128 * head_dim * 2 bytes (rotated K and
+ * transposed V; see regen_attn_workspace_size) and a scratch area for query
+ * tiles whose keys are split over several workgroups of the persistent
+ * attention kernel: 2 * P * 128 * (head_dim + 2) * 4 bytes, P = resident
+ * workgroups of the device (2 per compute unit on MI355X: 64.5 MiB at
+ * head_dim 128).
  * On success *out receives the handle; on any failure *out is set to NULL
  * (when out is not NULL) and the status says why:
  *   INVALID_ARGUMENT (NULL desc/out, wrong struct_size, heads/grid < 1,
@@ -137,20 +142,22 @@ const char *regen_attn_last_error(void);
 
 /*
  * Kernel timing for handles created with REGEN_ATTN_PROFILE. Each forward
- * then records HIP events on its stream before and after each of its two
- * kernels (the K-rotation / V-transpose pass and the attention kernel).
- * This call waits for the events of every forward issued since the last
- * read, adds their durations (milliseconds) to *prep_ms and *attn_ms and the
- * number of forwards to *calls (each output may be NULL), and forgets them.
+ * then records HIP events on its stream around each of its three kernels
+ * (the K-rotation / V-transpose pass, the attention kernel, the merge of
+ * tiles split across workgroups). This call waits for the events of every
+ * forward issued since the last read, adds their durations (milliseconds)
+ * to *prep_ms, *attn_ms, *merge_ms and the number of forwards to *calls
+ * (each output may be NULL), and forgets them.
  * Errors: INVALID_ARGUMENT (handle not live, or created without the flag),
  * HIP (event failure).
  */
 regen_status regen_attn_profile_read(regen_attn_t h, double *prep_ms, double *attn_ms,
-                                     int64_t *calls);
+                                     double *merge_ms, int64_t *calls);
 
 /*
- * Workspace bytes regen_attn_create would allocate for desc, or 0 if the
- * description is invalid. Touches no device.
+ * Bytes of the rotated-K / transposed-V workspace regen_attn_create would
+ * allocate for desc (the device-dependent split-tile scratch not included),
+ * or 0 if the description is invalid. Touches no device.
  */
 size_t regen_attn_workspace_size(const regen_attn_desc *desc);
 
