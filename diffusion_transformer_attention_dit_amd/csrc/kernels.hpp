@@ -222,33 +222,61 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_
 }
 
 // ---------------------------------------------------------------------------
-// Work schedule (stream-K style). A "unit" is one (query tile, key block)
-// pair: query tile t (BM = 32 NW rows of one head) against key block b (BN
-// keys); unit index x = t * nkv + b, tiles numbered head-major. The P
-// persistent workgroups take equal contiguous unit ranges, so every
-// resident slot of the GPU gets the same work whatever the tile count. A
-// tile whose units span several workgroups is finished by the merge kernel
-// from the per-workgroup partial results (unnormalised O, running max m,
-// row sum l), combined exactly as in blockwise softmax.
+// Work schedule. A "unit" is one (query tile, key block) pair: query tile t
+// (BM = 32 NW rows of one head; tiles numbered head-major) against key
+// block b (BN keys); unit index x = t * nkv + b. P persistent workgroups
+// (one full round of resident slots) first make `full` passes over whole
+// tiles, pass i giving tile i * P + p to workgroup p, so the workgroups that
+// share an XCD sweep the same head's keys together. The `rem` leftover
+// tiles (tiles >= full * P) are then cut stream-K style: their units are
+// split into P equal contiguous ranges, one per workgroup, so every slot
+// ends with the same amount of work. A leftover tile whose units span
+// several workgroups is finished by the merge kernel from the per-workgroup
+// partial results (unnormalised O, running max m, row sum l), combined
+// exactly as in blockwise softmax.
 // ---------------------------------------------------------------------------
 struct Sched {
-    int n_qtiles;     // query tiles per head
-    int nkv;          // key blocks per tile
-    long long units;  // heads * n_qtiles * nkv
-    int P;            // persistent workgroups (1 <= P <= units)
+    int n_qtiles;         // query tiles per head
+    int nkv;              // key blocks per tile
+    int P;                // persistent workgroups
+    int full;             // whole-tile passes
+    long long rem_units;  // units of the leftover tiles (rem * nkv)
 };
 
-__device__ __forceinline__ long long unit_begin(const Sched& sc, int p) {
-    return (long long)p * sc.units / sc.P;
+// Start (offset into the leftover units) of workgroup p's leftover range.
+__device__ __forceinline__ long long rem_begin(const Sched& sc, int p) {
+    return (long long)p * sc.rem_units / sc.P;
 }
-// The workgroup whose range holds unit x.
-__device__ __forceinline__ int unit_owner(const Sched& sc, long long x) {
-    return (int)(((x + 1) * sc.P - 1) / sc.units);
+// The workgroup whose leftover range holds leftover unit y.
+__device__ __forceinline__ int rem_owner(const Sched& sc, long long y) {
+    return (int)(((y + 1) * sc.P - 1) / sc.rem_units);
 }
-// Partial-result slot of workgroup p for tile t: its first tile uses 2p, a
-// later (necessarily last) tile uses 2p + 1.
+// Partial-result slot of workgroup p for leftover tile t: the first tile of
+// its range uses 2p, a later (necessarily its last) tile uses 2p + 1.
 __device__ __forceinline__ int partial_slot(const Sched& sc, int p, long long t) {
-    return (t == unit_begin(sc, p) / sc.nkv) ? 2 * p : 2 * p + 1;
+    const long long x0 = (long long)sc.full * sc.P * sc.nkv + rem_begin(sc, p);
+    return (t == x0 / sc.nkv) ? 2 * p : 2 * p + 1;
+}
+
+// Segment k of workgroup p's work: tile *t, key blocks [*kv0, *kv1).
+// Returns false past the last segment.
+__device__ __forceinline__ bool get_segment(const Sched& sc, int p, int k, long long* t, int* kv0,
+                                            int* kv1) {
+    if (k < sc.full) {
+        *t = (long long)k * sc.P + p;
+        *kv0 = 0;
+        *kv1 = sc.nkv;
+        return true;
+    }
+    const long long base = (long long)sc.full * sc.P * sc.nkv;
+    const long long a = base + rem_begin(sc, p), b = base + rem_begin(sc, p + 1);
+    const long long x = (k == sc.full) ? a : (a / sc.nkv + (k - sc.full)) * sc.nkv;
+    if (x >= b) return false;
+    *t = x / sc.nkv;
+    *kv0 = (int)(x - *t * sc.nkv);
+    const long long left = b - x;
+    *kv1 = (left < (long long)(sc.nkv - *kv0)) ? *kv0 + (int)left : sc.nkv;
+    return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -278,32 +306,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // Consecutive logical workgroups (hence consecutive tiles of one head)
     // share an XCD and its L2.
     const int pid = xcd_remap(blockIdx.x, gridDim.x);
-    const long long u0 = unit_begin(sc, pid), u1 = unit_begin(sc, pid + 1);
-    if (u0 >= u1) return;  // uniform over the block; no barrier reached yet
-    const long long first_tile = u0 / sc.nkv;
+    long long t;
+    int kv0, kv1;
+    if (!get_segment(sc, pid, 0, &t, &kv0, &kv1)) return;  // uniform; no barrier reached yet
 
     const uint32_t head_bytes = (uint32_t)Npad * D * 2;
     const int HW = geo.H * geo.W;
 
-    // Copy the K/V block of unit (tile t, block b) into LDS buffer `buf`.
-    auto issue_unit = [&](long long t, int b, int buf) {
-        const int h = (int)(t / sc.n_qtiles);
+    // Copy the K/V block of unit (tile tt, block b) into LDS buffer `buf`.
+    auto issue_unit = [&](long long tt, int b, int buf) {
+        const int h = (int)(tt / sc.n_qtiles);
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(kr + (size_t)h * Npad * D, head_bytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt + (size_t)h * Npad * D, head_bytes);
         char* ks = smem + buf * (KBYTES + VBYTES);
         issue_tile<D, BN, NW>(krs, vrs, b, ks, ks + KBYTES, wave, lane);
     };
 
-    issue_unit(first_tile, (int)(u0 - first_tile * sc.nkv), 0);
+    issue_unit(t, kv0, 0);
     int buf = 0;
-    long long u = u0;
+    bool more = true;
 
-    while (u < u1) {
-        // ---- one segment: tile t, key blocks [kv0, kv1) ----
-        const long long t = u / sc.nkv;
-        const int kv0 = (int)(u - t * sc.nkv);
-        const long long seg_end = ((t + 1) * sc.nkv < u1) ? (t + 1) * sc.nkv : u1;
-        const int kv1 = kv0 + (int)(seg_end - u);
+    for (int k = 0; more; ++k) {
+        // ---- segment k: tile t, key blocks [kv0, kv1) ----
+        long long nt_ = 0;
+        int nkv0 = 0, nkv1 = 0;
+        more = get_segment(sc, pid, k + 1, &nt_, &nkv0, &nkv1);
         const int hd = (int)(t / sc.n_qtiles), qt = (int)(t % sc.n_qtiles);
         const int qrow = qt * BM + wave * 32 + col;
 
@@ -340,18 +367,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int i = 0; i < 16; ++i) negm[i] = 0.0f;
         float l0 = 0.0f, l1 = 0.0f;  // this lane's partial row sums
 
-        if (u == u0) {
+        if (k == 0) {
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
 
-        for (int b = kv0; b < kv1; ++b, ++u) {
+        for (int b = kv0; b < kv1; ++b) {
             const char* ks = smem + buf * (KBYTES + VBYTES);
             const char* vs = ks + KBYTES;
-            if (u + 1 < u1) {
-                const bool same = b + 1 < sc.nkv;
-                issue_unit(same ? t : t + 1, same ? b + 1 : 0, buf ^ 1);
-            }
+            if (b + 1 < kv1)
+                issue_unit(t, b + 1, buf ^ 1);
+            else if (more)
+                issue_unit(nt_, nkv0, buf ^ 1);
 
             // MFMA A operands come from LDS through a ring of RING fragments
             // read ahead of their use: fragments 0..NK-1 are the K tile (key
@@ -506,13 +533,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             if (half == 0)
                 *reinterpret_cast<float2*>(part_ml + ((size_t)slot * BM + r) * 2) = make_float2(m_run, l_row);
         }
+        t = nt_;
+        kv0 = nkv0;
+        kv1 = nkv1;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 3: merge of split tiles. Grid heads * n_qtiles, 256 threads; a tile
-// held whole by one workgroup returns at once. Row r of a split tile:
-//   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Kernel 3: merge of split leftover tiles. Grid (rem tiles, BM): one block
+// per query row, 256 threads = 8 segment lanes x 32 groups of D/32 head
+// dims. A tile held whole by one workgroup returns at once. For row r:
+//   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s;
+// each segment lane folds every 8th segment, then the 8 lanes combine
+// through LDS the same way.
 // ---------------------------------------------------------------------------
 template <int D, int NW>
 __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o,
@@ -520,51 +553,66 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o,
                                                     const float* __restrict__ part_ml, int N,
                                                     Sched sc) {
     constexpr int BM = NW * 32;
-    constexpr int TPR = 256 / BM;  // threads per row
-    constexpr int DPT = D / TPR;   // head dims per thread
-    static_assert(DPT % 4 == 0, "vector width");
-    const long long t = blockIdx.x;
-    const int p0 = unit_owner(sc, t * sc.nkv);
-    const int p1 = unit_owner(sc, (t + 1) * sc.nkv - 1);
-    if (p0 == p1) return;
+    constexpr int DPT = D / 32;  // head dims per thread (4 or 2)
+    const long long t = (long long)sc.full * sc.P + blockIdx.x;
+    const long long y0 = (long long)blockIdx.x * sc.nkv;  // leftover unit offsets of tile t
+    const int p0 = rem_owner(sc, y0);
+    const int p1 = rem_owner(sc, y0 + sc.nkv - 1);
+    if (p0 == p1) return;  // uniform over the block
     const int hd = (int)(t / sc.n_qtiles), qt = (int)(t % sc.n_qtiles);
-    const int r = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DPT;
+    const int r = blockIdx.y;
     const int qrow = qt * BM + r;
-    if (qrow >= N) return;
-    float M = -INFINITY;
-    for (int p = p0; p <= p1; ++p) {
-        const int slot = partial_slot(sc, p, t);
-        M = fmaxf(M, part_ml[((size_t)slot * BM + r) * 2]);
-    }
-    float acc[DPT];
+    if (qrow >= N) return;  // uniform over the block
+    const int sl = threadIdx.x / 32, d0 = (threadIdx.x % 32) * DPT;
+
+    float Mi = -INFINITY;
+    for (int p = p0 + sl; p <= p1; p += 8)
+        Mi = fmaxf(Mi, part_ml[((size_t)partial_slot(sc, p, t) * BM + r) * 2]);
+    float Li = 0.0f, acc[DPT];
 #pragma unroll
     for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
-    float L = 0.0f;
-    for (int p = p0; p <= p1; ++p) {
+    for (int p = p0 + sl; p <= p1; p += 8) {
         const int slot = partial_slot(sc, p, t);
         const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((size_t)slot * BM + r) * 2);
-        const float w = __builtin_amdgcn_exp2f(ml.x - M);
-        L += w * ml.y;
+        const float w = __builtin_amdgcn_exp2f(ml.x - Mi);
+        Li += w * ml.y;
         const float* po = part_o + ((size_t)slot * BM + r) * D + d0;
 #pragma unroll
-        for (int i = 0; i < DPT; i += 4) {
-            const float4 x = *reinterpret_cast<const float4*>(po + i);
-            acc[i] += w * x.x;
-            acc[i + 1] += w * x.y;
-            acc[i + 2] += w * x.z;
-            acc[i + 3] += w * x.w;
-        }
+        for (int i = 0; i < DPT; ++i) acc[i] += w * po[i];
+    }
+
+    __shared__ float sm[8][32][DPT + 2];
+    sm[sl][threadIdx.x % 32][0] = Mi;
+    sm[sl][threadIdx.x % 32][1] = Li;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) sm[sl][threadIdx.x % 32][2 + i] = acc[i];
+    __syncthreads();
+    if (sl != 0) return;
+    const int g = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) M = fmaxf(M, sm[k][g][0]);
+    float L = 0.0f, out[DPT];
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) out[i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float Mk = sm[k][g][0];
+        if (Mk == -INFINITY) continue;  // lane without segments
+        const float w = __builtin_amdgcn_exp2f(Mk - M);
+        L += w * sm[k][g][1];
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) out[i] += w * sm[k][g][2 + i];
     }
     const float inv = 1.0f / L;
     uint16_t* op = o + ((size_t)hd * N + qrow) * D + d0;
-#pragma unroll
-    for (int i = 0; i < DPT; i += 8) {
-        uint4 w4;
-        w4.x = pack_bf16(acc[i] * inv, acc[i + 1] * inv);
-        w4.y = pack_bf16(acc[i + 2] * inv, acc[i + 3] * inv);
-        w4.z = pack_bf16(acc[i + 4] * inv, acc[i + 5] * inv);
-        w4.w = pack_bf16(acc[i + 6] * inv, acc[i + 7] * inv);
-        *reinterpret_cast<uint4*>(op + i) = w4;
+    if constexpr (DPT == 4) {
+        uint2 w2;
+        w2.x = pack_bf16(out[0] * inv, out[1] * inv);
+        w2.y = pack_bf16(out[2] * inv, out[3] * inv);
+        *reinterpret_cast<uint2*>(op) = w2;
+    } else {
+        *reinterpret_cast<uint32_t*>(op) = pack_bf16(out[0] * inv, out[1] * inv);
     }
 }
 

@@ -294,12 +294,15 @@ regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, co
     const float c2 = p.scale * 1.4426950408889634f;
 
     dim3 pgrid(unsigned(Npad / regen::kPrepKeys), unsigned(p.heads));
+    const int64_t tiles = int64_t(p.heads) * p.n_qtiles;
     regen::Sched sc;
     sc.n_qtiles = p.n_qtiles;
     sc.nkv = p.nkv;
-    sc.units = p.units;
     sc.P = h->P;
-    const unsigned mgrid = unsigned(p.heads) * unsigned(p.n_qtiles);
+    sc.full = int(tiles / h->P);
+    const int64_t rem_tiles = tiles - int64_t(sc.full) * h->P;
+    sc.rem_units = rem_tiles * p.nkv;
+    const dim3 mgrid{unsigned(rem_tiles), unsigned(kBM), 1u};
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
     const uint16_t* k16 = static_cast<const uint16_t*>(k);
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
@@ -334,8 +337,9 @@ regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, co
                            st, q16, h->d_kr, h->d_vt, o16, h->d_tab, h->geo, N, Npad, sc, c2,
                            h->d_part_o, h->d_part_ml);
         mark(2);
-        hipLaunchKernelGGL((regen::merge_kernel<128, kNW>), dim3(mgrid), dim3(256), 0, st, o16,
-                           h->d_part_o, h->d_part_ml, N, sc);
+        if (rem_tiles > 0)
+            hipLaunchKernelGGL((regen::merge_kernel<128, kNW>), mgrid, dim3(256), 0, st, o16,
+                               h->d_part_o, h->d_part_ml, N, sc);
     } else {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
                            h->d_vt, h->d_tab, h->geo, N, Npad);
@@ -344,8 +348,9 @@ regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, co
                            st, q16, h->d_kr, h->d_vt, o16, h->d_tab, h->geo, N, Npad, sc, c2,
                            h->d_part_o, h->d_part_ml);
         mark(2);
-        hipLaunchKernelGGL((regen::merge_kernel<64, kNW>), dim3(mgrid), dim3(256), 0, st, o16,
-                           h->d_part_o, h->d_part_ml, N, sc);
+        if (rem_tiles > 0)
+            hipLaunchKernelGGL((regen::merge_kernel<64, kNW>), mgrid, dim3(256), 0, st, o16,
+                               h->d_part_o, h->d_part_ml, N, sc);
     }
     hipError_t e = hipGetLastError();
     if (prof) {
