@@ -6,10 +6,13 @@
 //     embedding to K and rounds it to bf16 into a padded row-major copy Kr,
 //     and writes V transposed into Vt, a key-contiguous layout that the P V
 //     matrix product can feed straight from LDS as MFMA operands.
-//  2. attn_fwd_kernel (MFMA-bound): flash-style exact attention. Each wave
-//     owns 32 query rows, rotates its Q rows while loading them (RoPE on
-//     load), then streams K/V tiles through double-buffered LDS and keeps
-//     the online softmax (running max, running sum) in registers.
+//  2. attn_fwd_kernel (MFMA-bound): flash-style exact attention, persistent
+//     (one round of resident workgroups, see Sched). Each wave owns 32 query
+//     rows, rotates its Q rows while loading them (RoPE on load), then
+//     streams K/V blocks through double-buffered LDS and keeps the online
+//     softmax (running max, running sum) in registers.
+//  3. merge_kernel: finishes query tiles whose key blocks were split over
+//     several workgroups.
 //
 // The attention is the one ReGenVC's decoder transformer evaluates over the
 // window's latent tokens (arXiv 2607.28144, blog summary "Methodology - deep

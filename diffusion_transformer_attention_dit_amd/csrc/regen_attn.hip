@@ -19,7 +19,7 @@ namespace {
 
 constexpr uint32_t kKnownFlags = REGEN_ATTN_NO_ROPE | REGEN_ATTN_PROFILE;
 // Attention kernel shape: NW waves of 32 query rows, BN-key blocks.
-constexpr int kNW = 4, kBM = kNW * 32, kBN = 64;
+constexpr int kNW = 8, kBM = kNW * 32, kBN = 64;
 constexpr int64_t kMaxTokens = int64_t(1) << 30;
 
 thread_local std::string g_last_error;
