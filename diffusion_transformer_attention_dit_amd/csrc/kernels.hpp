@@ -316,16 +316,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const uint32_t head_bytes = (uint32_t)Npad * D * 2;
     const int HW = geo.H * geo.W;
 
-    // Copy the K/V block of unit (tile tt, block b) into LDS buffer `buf`.
-    auto issue_unit = [&](long long tt, int b, int buf) {
-        const int h = (int)(tt / sc.n_qtiles);
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kr + (size_t)h * Npad * D, head_bytes);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt + (size_t)h * Npad * D, head_bytes);
-        char* ks = smem + buf * (KBYTES + VBYTES);
-        issue_tile<D, BN, NW>(krs, vrs, b, ks, ks + KBYTES, wave, lane);
+    // Buffer resources over the Kr rows and Vt blocks of tile tt's head.
+    auto head_rsrc = [&](long long tt, __amdgpu_buffer_rsrc_t* krs, __amdgpu_buffer_rsrc_t* vrs) {
+        const int h = (int)tt / sc.n_qtiles;
+        *krs = make_rsrc(kr + (size_t)h * Npad * D, head_bytes);
+        *vrs = make_rsrc(vt + (size_t)h * Npad * D, head_bytes);
     };
-
-    issue_unit(t, kv0, 0);
+    __amdgpu_buffer_rsrc_t krs, vrs;
+    head_rsrc(t, &krs, &vrs);
+    issue_tile<D, BN, NW>(krs, vrs, kv0, smem, smem + KBYTES, wave, lane);
     int buf = 0;
     bool more = true;
 
@@ -334,7 +333,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         long long nt_ = 0;
         int nkv0 = 0, nkv1 = 0;
         more = get_segment(sc, pid, k + 1, &nt_, &nkv0, &nkv1);
-        const int hd = (int)(t / sc.n_qtiles), qt = (int)(t % sc.n_qtiles);
+        __amdgpu_buffer_rsrc_t nkrs = krs, nvrs = vrs;  // the next segment's head
+        if (more) head_rsrc(nt_, &nkrs, &nvrs);
+        const int hd = (int)t / sc.n_qtiles, qt = (int)t - hd * sc.n_qtiles;
         const int qrow = qt * BM + wave * 32 + col;
 
         // Q: load this lane's half-rows, rotate them (RoPE on load) and fold
@@ -378,10 +379,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int b = kv0; b < kv1; ++b) {
             const char* ks = smem + buf * (KBYTES + VBYTES);
             const char* vs = ks + KBYTES;
-            if (b + 1 < kv1)
-                issue_unit(t, b + 1, buf ^ 1);
-            else if (more)
-                issue_unit(nt_, nkv0, buf ^ 1);
+            {
+                char* nks = smem + (buf ^ 1) * (KBYTES + VBYTES);
+                if (b + 1 < kv1)
+                    issue_tile<D, BN, NW>(krs, vrs, b + 1, nks, nks + KBYTES, wave, lane);
+                else if (more)
+                    issue_tile<D, BN, NW>(nkrs, nvrs, nkv0, nks, nks + KBYTES, wave, lane);
+            }
 
             // MFMA A operands come from LDS through a ring of RING fragments
             // read ahead of their use: fragments 0..NK-1 are the K tile (key
@@ -402,7 +406,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int f = 0; f < RING; ++f) fr[f] = frag(f);
 
-            // S^T = K Q^T - m_run for this block: BN keys x 32 queries.
+            // S^T = K Q^T - m_run for this block: BN keys x 32 queries. The
+            // wave issuing these MFMAs gets issue priority, so the other wave
+            // on its SIMD runs its softmax meanwhile rather than both waves
+            // reaching the softmax together.
+            __builtin_amdgcn_s_setprio(2);
             f32x16 s[BN / 32];
 #pragma unroll
             for (int f = 0; f < NK; ++f) {
@@ -412,6 +420,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 if (f + RING < NK + NV) fr[f % RING] = frag(f + RING);
             }
 
+            __builtin_amdgcn_s_setprio(0);
             // Keys past the end of the sequence get -inf (never zero-padding).
             if (b == sc.nkv - 1 && (N % BN) != 0) {
 #pragma unroll
@@ -539,6 +548,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         t = nt_;
         kv0 = nkv0;
         kv1 = nkv1;
+        krs = nkrs;
+        vrs = nvrs;
     }
 }
 
