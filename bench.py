@@ -29,7 +29,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="window25_12x128_n10920")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run 3 device-to-device copies of this many MiB (to scale HBM "
@@ -48,6 +48,26 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n * 4,
                                            "bytes_written_per_copy": n * 4, "copies": 3}}))
     return 0
+
+
+def counted_traffic(w, algorithmic_bytes):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    passes (FETCH_SIZE, WRITE_SIZE, scaled against a copy of known size), or
+    None when the kernel source has changed since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_%s_traffic.json" % w.name)
+    src = os.path.join(ROOT, "diffusion_transformer_attention_dit_amd", "csrc", "kernels.hpp")
+    try:
+        doc = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if doc.get("kernel_source_sha256") != sha:
+        return None
+    total = doc["fetch_bytes_per_launch"] + doc["write_bytes_per_launch"]
+    return {"bytes_per_launch": round(total), "read_bytes": round(doc["fetch_bytes_per_launch"]),
+            "write_bytes": round(doc["write_bytes_per_launch"]),
+            "vs_algorithmic": round(total / algorithmic_bytes, 3)}
 
 
 def cpu_baseline(w, target_s):
@@ -103,7 +123,7 @@ def _cpu_model():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build carries no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
     import torch
@@ -160,6 +180,7 @@ def main():
     merge_avg_s = merge_ms / n_calls * 1e-3
     attn_tflops = w.flops_per_call / attn_avg_s / 1e12
     prep_bytes = 4 * w.heads * w.tokens * w.head_dim * 2  # read K, V; write Kr, Vt
+    traffic = counted_traffic(w, w.bytes_per_call)
 
     line = {
         "metric": METRIC,
@@ -190,7 +211,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": (traffic or {}).get("bytes_per_launch"),
+            "traffic_detail": traffic,
             "avg_launch_us": round(attn_avg_s * 1e6, 2),
             "launches": n_calls,
         },
