@@ -388,15 +388,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
 
             // MFMA A operands come from LDS through a ring of RING fragments
-            // read ahead of their use: fragments 0..NK-1 are the K tile (key
-            // block kk, head-dim block kb), NK..NK+NV-1 the Vt tile (head-dim
-            // block db, key block kq). The first Vt fragments are requested
-            // during the S products, before the softmax needs them.
+            // read ahead of their use: fragments 0..NK-1 are the K tile (head-
+            // dim block kb major, key block kk minor, so consecutive S MFMAs
+            // feed different accumulators), NK..NK+NV-1 the Vt tile (head-dim
+            // block db, key block kq). LDS read bandwidth is close to what the
+            // S products need while all waves run them at once, so the first
+            // Vt fragments are requested after the S products, to land during
+            // the softmax.
             constexpr int KB = D / 16, NK = (BN / 32) * KB, QB16 = BN / 16, NV = (D / 32) * QB16;
             constexpr int RING = 8;
             auto frag = [&](int f) -> bf16x8 {
                 if (f < NK) {
-                    const int kk = f / KB, kb = f % KB;
+                    const int kk = f % (BN / 32), kb = f / (BN / 32);
                     return *reinterpret_cast<const bf16x8*>(ks + swz_off<KRB>(kk * 32 + col, kb * 2 + half));
                 }
                 const int g = f - NK, db = g / QB16, kq = g % QB16;
@@ -414,11 +417,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             f32x16 s[BN / 32];
 #pragma unroll
             for (int f = 0; f < NK; ++f) {
-                const int kk = f / KB, kb = f % KB;
+                const int kk = f % (BN / 32), kb = f / (BN / 32);
                 s[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % RING], qf[kb],
                                                                 kb == 0 ? negm : s[kk], 0, 0, 0);
-                if (f + RING < NK + NV) fr[f % RING] = frag(f + RING);
+                if (f + RING < NK) fr[f % RING] = frag(f + RING);
             }
+#pragma unroll
+            for (int f = NK; f < NK + RING; ++f) fr[f % RING] = frag(f);
 
             __builtin_amdgcn_s_setprio(0);
             // Keys past the end of the sequence get -inf (never zero-padding).
