@@ -58,6 +58,12 @@ def load():
     lib.oracle_attention.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int64,
                                      ctypes.c_int64, ctypes.c_int, ctypes.c_double]
     lib.oracle_attention.restype = ctypes.c_int
+    lib.oracle_attention_lse.argtypes = [dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int, ctypes.c_double]
+    lib.oracle_attention_lse.restype = ctypes.c_int
+    lib.oracle_merge.argtypes = [ctypes.POINTER(dp), ctypes.POINTER(dp), ctypes.c_int,
+                                 ctypes.c_int64, ctypes.c_int, dp, dp]
+    lib.oracle_merge.restype = ctypes.c_int
     lib.oracle_token_coords.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                         i64p, i64p, i64p]
     lib.oracle_token_coords.restype = None
@@ -128,8 +134,11 @@ def c_rope_positions(x, pos, pairs=None, base=10000.0):
     return y
 
 
-def c_attention(q, k, v, scale=None):
-    """Exact attention of queries q [heads, R, d] against all keys k, v."""
+def c_attention(q, k, v, scale=None, return_lse=False):
+    """Exact attention of queries q [heads, R, d] against all keys k, v.
+
+    With return_lse, also the log-sum-exp of each row's scores [heads, R]
+    (natural log, scores including the scale)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     heads, r, d = q.shape
     n = k.shape[1]
@@ -137,11 +146,36 @@ def c_attention(q, k, v, scale=None):
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = np.empty((heads, r, d), dtype=np.float64)
-    rc = load().oracle_attention(_dptr(q), _dptr(k), _dptr(v), _dptr(o), heads, r, n, d,
-                                 float(scale))
+    lse = np.empty((heads, r), dtype=np.float64) if return_lse else None
+    rc = load().oracle_attention_lse(_dptr(q), _dptr(k), _dptr(v), _dptr(o),
+                                     _dptr(lse) if return_lse else None, heads, r, n, d,
+                                     float(scale))
     if rc != 0:
-        raise ValueError("oracle_attention failed (rc=%d)" % rc)
-    return o
+        raise ValueError("oracle_attention_lse failed (rc=%d)" % rc)
+    return (o, lse) if return_lse else o
+
+
+def c_merge(o_parts, lse_parts):
+    """Combine attention results over disjoint key sets (C oracle).
+
+    o_parts: list of [..., d] arrays; lse_parts: matching [...] arrays.
+    Returns (o, lse) over the union of the key sets."""
+    o_parts = [_f64(o) for o in o_parts]
+    lse_parts = [_f64(l) for l in lse_parts]
+    shape = o_parts[0].shape
+    d = shape[-1]
+    rows = int(np.prod(shape[:-1]))
+    for o, l in zip(o_parts, lse_parts):
+        assert o.shape == shape and l.shape == shape[:-1]
+    dp = ctypes.POINTER(ctypes.c_double)
+    op = (dp * len(o_parts))(*[_dptr(o) for o in o_parts])
+    lp = (dp * len(lse_parts))(*[_dptr(l) for l in lse_parts])
+    o = np.empty(shape, dtype=np.float64)
+    lse = np.empty(shape[:-1], dtype=np.float64)
+    rc = load().oracle_merge(op, lp, len(o_parts), rows, d, _dptr(o), _dptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_merge failed (rc=%d)" % rc)
+    return o, lse
 
 
 def grid_positions(rows, grid):
@@ -150,11 +184,12 @@ def grid_positions(rows, grid):
 
 
 def rope_attention(q, k, v, grid, pairs=None, base=10000.0, scale=None, rows=None,
-                   rope=True):
+                   rope=True, return_lse=False):
     """The whole hot path in fp64: rotate Q and K over the latent grid, then
     exact softmax attention, for the query rows listed (all rows if None).
 
-    Returns [heads, len(rows), d] (or [heads, N, d])."""
+    Returns [heads, len(rows), d] (or [heads, N, d]), and with return_lse the
+    rows' log-sum-exp [heads, len(rows)] too."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     heads, n, d = q.shape
     if rows is not None:
@@ -167,7 +202,29 @@ def rope_attention(q, k, v, grid, pairs=None, base=10000.0, scale=None, rows=Non
             pos = np.tile(grid_positions(rows, grid), (heads, 1))
             q = c_rope_positions(q.reshape(-1, d), pos, pairs, base).reshape(q.shape)
         k = c_rope_grid(k, grid, pairs, base)
-    return c_attention(q, k, v, scale)
+    return c_attention(q, k, v, scale, return_lse)
+
+
+def rope_attention_range(q, k, v, grid, q_begin, kv_begin, pairs=None, base=10000.0,
+                         scale=None, rows=None, rope=True):
+    """Attention of a run of query tokens against a run of key tokens of one
+    window, each rotated at its own place on the latent grid.
+
+    q: [heads, nq, d] holds tokens q_begin .. q_begin+nq-1; k, v:
+    [heads, nk, d] hold tokens kv_begin .. kv_begin+nk-1. rows (indices into
+    q's nq rows) picks a sample of query rows. Returns (o [heads, R, d],
+    lse [heads, R])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    heads, nq, d = q.shape
+    nk = k.shape[1]
+    rows = np.arange(nq, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    q = np.ascontiguousarray(q[:, rows, :])
+    if rope:
+        qpos = np.tile(grid_positions(rows + q_begin, grid), (heads, 1))
+        q = c_rope_positions(q.reshape(-1, d), qpos, pairs, base).reshape(q.shape)
+        kpos = np.tile(grid_positions(np.arange(nk) + kv_begin, grid), (heads, 1))
+        k = c_rope_positions(k.reshape(-1, d), kpos, pairs, base).reshape(k.shape)
+    return c_attention(q, k, v, scale, return_lse=True)
 
 
 # ---------------------------------------------------------------------------
@@ -217,6 +274,18 @@ def np_attention(q, k, v, scale=None, return_probs=False):
     p = p / p.sum(axis=-1, keepdims=True)
     o = np.matmul(p, v)
     return (o, p) if return_probs else o
+
+
+def np_merge(o_parts, lse_parts):
+    """Combine results over disjoint key sets, written a second way: the
+    part weights are a softmax over the stacked LSEs."""
+    lse = np.stack([np.asarray(l, dtype=np.float64) for l in lse_parts])  # [P, ...]
+    o = np.stack([np.asarray(x, dtype=np.float64) for x in o_parts])      # [P, ..., d]
+    top = lse.max(axis=0)
+    w = np.exp(lse - top)
+    z = w.sum(axis=0)
+    merged = (w[..., None] * o).sum(axis=0) / z[..., None]
+    return merged, top + np.log(z)
 
 
 def np_rope_attention(q, k, v, grid, pairs=None, base=10000.0, scale=None, rope=True):

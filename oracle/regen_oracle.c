@@ -117,17 +117,22 @@ int oracle_rope_grid(const double *x, double *y, int heads, int head_dim,
 }
 
 /*
- * Exact softmax attention.
+ * Exact softmax attention, optionally with the log-sum-exp of the scores.
  *   q : [heads][n_q][head_dim]     (any subset of query rows, already rotated)
  *   k : [heads][n_kv][head_dim]    v : [heads][n_kv][head_dim]
- *   o : [heads][n_q][head_dim]
+ *   o : [heads][n_q][head_dim]     lse : [heads][n_q] or NULL
  * For each (head, query row m): s_n = scale * <q_m, k_n> over all n_kv keys,
- * p_n = exp(s_n - max s) / sum exp(s - max s), o_m = sum_n p_n v_n.
+ * p_n = exp(s_n - max s) / sum exp(s - max s), o_m = sum_n p_n v_n and
+ * lse_m = log sum_n exp(s_n) = max s + log sum exp(s - max s). The LSE is what
+ * the Ring half of USP needs to combine attention over separate key chunks
+ * exactly (blog summary, "Methodology - deep read", USP paragraph: Ring
+ * passes key/value blocks around; "Technical innovations": the result stays
+ * exact).
  * Returns 0, or -1 on a bad argument, -2 if memory runs out.
  */
-int oracle_attention(const double *q, const double *k, const double *v,
-                     double *o, int heads, int64_t n_q, int64_t n_kv,
-                     int head_dim, double scale) {
+int oracle_attention_lse(const double *q, const double *k, const double *v,
+                         double *o, double *lse, int heads, int64_t n_q,
+                         int64_t n_kv, int head_dim, double scale) {
     if (!q || !k || !v || !o || heads < 1 || n_q < 0 || n_kv < 1 ||
         head_dim < 1)
         return -1;
@@ -165,11 +170,62 @@ int oracle_attention(const double *q, const double *k, const double *v,
                 }
                 double *om = o + ((int64_t)hd * n_q + m) * head_dim;
                 for (int c = 0; c < head_dim; ++c) om[c] = acc[c] / den;
+                if (lse) lse[(int64_t)hd * n_q + m] = mx + log(den);
             }
         free(s);
         free(acc);
     }
     return failed ? -2 : 0;
+}
+
+/* Exact softmax attention without the LSE (see oracle_attention_lse). */
+int oracle_attention(const double *q, const double *k, const double *v,
+                     double *o, int heads, int64_t n_q, int64_t n_kv,
+                     int head_dim, double scale) {
+    return oracle_attention_lse(q, k, v, o, NULL, heads, n_q, n_kv, head_dim,
+                                scale);
+}
+
+/*
+ * Combine attention results over disjoint key sets into the result over
+ * their union. Part i holds o_i = sum_{n in K_i} e^{s_n} v_n / Z_i and
+ * lse_i = log Z_i with Z_i = sum_{n in K_i} e^{s_n}; over the union,
+ * Z = sum_i Z_i, so lse = log sum_i e^{lse_i} and o = sum_i (Z_i / Z) o_i.
+ * A part with lse_i = -inf (no keys) has weight 0.
+ *   o_parts   : nparts arrays [rows][head_dim]
+ *   lse_parts : nparts arrays [rows]
+ *   o : [rows][head_dim], lse : [rows] or NULL
+ * Returns 0, or -1 on a bad argument (including a row where every part is
+ * -inf).
+ */
+int oracle_merge(const double *const *o_parts, const double *const *lse_parts,
+                 int nparts, int64_t rows, int head_dim, double *o,
+                 double *lse) {
+    if (!o_parts || !lse_parts || nparts < 1 || rows < 0 || head_dim < 1 || !o)
+        return -1;
+    for (int i = 0; i < nparts; ++i)
+        if (!o_parts[i] || !lse_parts[i]) return -1;
+    int bad = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        double mx = -INFINITY;
+        for (int i = 0; i < nparts; ++i)
+            if (lse_parts[i][r] > mx) mx = lse_parts[i][r];
+        if (mx == -INFINITY) {
+            bad = 1;
+            continue;
+        }
+        double z = 0.0;
+        for (int i = 0; i < nparts; ++i) z += exp(lse_parts[i][r] - mx);
+        double *orow = o + r * head_dim;
+        for (int c = 0; c < head_dim; ++c) orow[c] = 0.0;
+        for (int i = 0; i < nparts; ++i) {
+            double w = exp(lse_parts[i][r] - mx) / z;
+            const double *oi = o_parts[i] + r * head_dim;
+            for (int c = 0; c < head_dim; ++c) orow[c] += w * oi[c];
+        }
+        if (lse) lse[r] = mx + log(z);
+    }
+    return bad ? -1 : 0;
 }
 
 /* Number of threads a parallel region of this library will use. */

@@ -297,3 +297,138 @@ def test_golden_closed_form_fixture():
                                       base=g["base"])
     assert np.max(np.abs(got_c - o)) < 1e-13
     assert np.max(np.abs(got_np - o)) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# Log-sum-exp output and the merge of results over disjoint key sets (what
+# the Ring half of USP needs to stay exact: blog summary, "Methodology - deep
+# read", USP paragraph, and "Technical innovations").
+# --------------------------------------------------------------------------
+
+def test_lse_zero_query_is_log_n_exactly():
+    # q = 0: every score is 0, so lse = log(n_kv) and o = mean(v).
+    n = 37
+    q = np.zeros((2, 3, 16))
+    k, v = _rand(2, n, 16), _rand(2, n, 16)
+    o, lse = oracle.c_attention(q, k, v, return_lse=True)
+    assert np.array_equal(lse, np.full((2, 3), math.log(n)))
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=1, keepdims=True), o.shape),
+                               rtol=0, atol=1e-14)
+
+
+def test_lse_single_key_is_the_score():
+    q, k, v = _rand(1, 4, 8), _rand(1, 1, 8), _rand(1, 1, 8)
+    o, lse = oracle.c_attention(q, k, v, scale=0.3, return_lse=True)
+    np.testing.assert_allclose(lse, 0.3 * (q @ k.transpose(0, 2, 1))[..., 0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o, np.broadcast_to(v, o.shape), rtol=0, atol=1e-15)
+
+
+def test_lse_identical_keys():
+    # n copies of one key: lse = s + log(n).
+    n = 50
+    q = _rand(1, 3, 8)
+    k = np.broadcast_to(_rand(1, 1, 8), (1, n, 8)).copy()
+    _, lse = oracle.c_attention(q, k, _rand(1, n, 8), return_lse=True)
+    s = (q @ k[:, :1].transpose(0, 2, 1))[..., 0] / math.sqrt(8)
+    np.testing.assert_allclose(lse, s + math.log(n), rtol=0, atol=1e-13)
+
+
+def test_lse_matches_scipy_logsumexp():
+    from scipy.special import logsumexp
+    q, k, v = _rand(3, 20, 32, scale=2.0), _rand(3, 45, 32, scale=2.0), _rand(3, 45, 32)
+    _, lse = oracle.c_attention(q, k, v, return_lse=True)
+    s = (q @ k.transpose(0, 2, 1)) / math.sqrt(32)
+    np.testing.assert_allclose(lse, logsumexp(s, axis=-1), rtol=0, atol=1e-12)
+
+
+def test_lse_large_logits_stay_finite():
+    q, k, v = _rand(1, 5, 16, scale=60.0), _rand(1, 30, 16, scale=60.0), _rand(1, 30, 16)
+    o, lse = oracle.c_attention(q, k, v, return_lse=True)
+    s = (q @ k.transpose(0, 2, 1)) / 4.0
+    assert np.all(np.isfinite(lse)) and np.all(np.isfinite(o))
+    # lse lies in [max s, max s + log n]
+    assert np.all(lse >= s.max(axis=-1) - 1e-9) and np.all(lse <= s.max(axis=-1) + math.log(30) + 1e-9)
+
+
+@pytest.mark.parametrize("cuts", [[17], [1], [44], [5, 20, 33], [10, 11, 12, 13]])
+def test_merge_of_key_chunks_equals_full_attention(cuts):
+    # Blockwise softmax: attention over all keys is the merge of attention
+    # over any partition of the keys into runs.
+    q, k, v = _rand(2, 9, 16), _rand(2, 45, 16), _rand(2, 45, 16)
+    o_full, lse_full = oracle.c_attention(q, k, v, return_lse=True)
+    edges = [0] + cuts + [45]
+    parts = [oracle.c_attention(q, k[:, a:b], v[:, a:b], return_lse=True)
+             for a, b in zip(edges[:-1], edges[1:])]
+    o, lse = oracle.c_merge([p[0] for p in parts], [p[1] for p in parts])
+    np.testing.assert_allclose(o, o_full, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_full, rtol=0, atol=1e-13)
+
+
+def test_merge_of_non_contiguous_key_sets():
+    # Any disjoint split works, not only runs: interleaved keys.
+    q, k, v = _rand(1, 6, 8), _rand(1, 30, 8), _rand(1, 30, 8)
+    o_full, lse_full = oracle.c_attention(q, k, v, return_lse=True)
+    a = oracle.c_attention(q, k[:, 0::2], v[:, 0::2], return_lse=True)
+    b = oracle.c_attention(q, k[:, 1::2], v[:, 1::2], return_lse=True)
+    o, lse = oracle.c_merge([a[0], b[0]], [a[1], b[1]])
+    np.testing.assert_allclose(o, o_full, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_full, rtol=0, atol=1e-13)
+
+
+def test_merge_special_cases():
+    o1, o2 = _rand(4, 8), _rand(4, 8)
+    l1, l2 = _rand(4), _rand(4)
+    # one part: identity
+    o, lse = oracle.c_merge([o1], [l1])
+    assert np.array_equal(o, o1) and np.array_equal(lse, l1)
+    # equal weights: the mean, lse + log 2
+    o, lse = oracle.c_merge([o1, o2], [l1, l1])
+    np.testing.assert_allclose(o, (o1 + o2) / 2, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, l1 + math.log(2), rtol=0, atol=1e-15)
+    # an empty part (lse = -inf) has no weight
+    o, lse = oracle.c_merge([o1, o2], [l1, np.full(4, -np.inf)])
+    np.testing.assert_allclose(o, o1, rtol=0, atol=0)
+    np.testing.assert_allclose(lse, l1, rtol=0, atol=0)
+    # order of the parts does not matter
+    a = oracle.c_merge([o1, o2], [l1, l2])
+    b = oracle.c_merge([o2, o1], [l2, l1])
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-15)
+    # a part 40 nats below the other is negligible
+    o, _ = oracle.c_merge([o1, o2], [l1, l1 - 40.0])
+    np.testing.assert_allclose(o, o1, rtol=0, atol=1e-15)
+
+
+def test_merge_rejects_all_empty_row():
+    with pytest.raises(ValueError):
+        oracle.c_merge([_rand(2, 4)], [np.array([0.0, -np.inf])])
+
+
+def test_c_merge_matches_numpy_merge():
+    o_parts = [_rand(3, 5, 16) for _ in range(4)]
+    lse_parts = [_rand(3, 5, scale=5.0) for _ in range(4)]
+    a = oracle.c_merge(o_parts, lse_parts)
+    b = oracle.np_merge(o_parts, lse_parts)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-13)
+
+
+def test_range_attention_matches_full_grid():
+    # Rotating a run of tokens at its own grid places equals slicing the
+    # rotation of the whole window: the ranged oracle agrees with the full
+    # one on the rows and keys it covers, and merging key halves restores
+    # the full result.
+    w = synth.WORKLOADS["tiny_1x64_n128"]
+    q, k, v = (t.double().numpy() for t in synth.make_qkv(w, 0, 0, device="cpu"))
+    o_full, lse_full = oracle.rope_attention(q, k, v, w.grid, return_lse=True)
+    qa, qb, ka, kb = 30, 90, 40, 128
+    o_r, lse_r = oracle.rope_attention_range(q[:, qa:qb], k[:, ka:kb], v[:, ka:kb], w.grid,
+                                             q_begin=qa, kv_begin=ka)
+    o_a, lse_a = oracle.rope_attention_range(q[:, qa:qb], k[:, :ka], v[:, :ka], w.grid,
+                                             q_begin=qa, kv_begin=0)
+    o_m, lse_m = oracle.c_merge([o_r, o_a], [lse_r, lse_a])
+    np.testing.assert_allclose(o_m, o_full[:, qa:qb], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_m, lse_full[:, qa:qb], rtol=0, atol=1e-12)
+    # and the NumPy brute force over the same key run
+    qr = oracle.np_rope(q, w.grid)[:, qa:qb]
+    kr = oracle.np_rope(k, w.grid)[:, ka:kb]
+    np.testing.assert_allclose(o_r, oracle.np_attention(qr, kr, v[:, ka:kb]), rtol=0, atol=1e-13)
