@@ -293,3 +293,40 @@ def np_rope_attention(q, k, v, grid, pairs=None, base=10000.0, scale=None, rope=
         q = np_rope(q, grid, pairs, base)
         k = np_rope(k, grid, pairs, base)
     return np_attention(q, k, v, scale)
+
+
+# ---------------------------------------------------------------------------
+# Ulysses layouts (blog summary, "Methodology - deep read", USP paragraph:
+# Ulysses turns sequence shards into head shards with an all-to-all). Plain
+# definitions, element by element in meaning: G devices, device s holding
+# tokens s*Nl .. (s+1)*Nl - 1 of all H heads before the exchange, and all N
+# tokens of heads g*H/G .. (g+1)*H/G - 1 after it.
+# ---------------------------------------------------------------------------
+
+def ulysses_pack(x, groups):
+    """x [Nl, H, d] -> send [G, Nl, H/G, d] with send[g, i, j] = x[i, g*H/G + j]."""
+    x = np.asarray(x)
+    nl, h, d = x.shape
+    hg = h // groups
+    assert hg * groups == h
+    send = np.empty((groups, nl, hg, d), dtype=x.dtype)
+    for g in range(groups):
+        send[g] = x[:, g * hg:(g + 1) * hg, :]
+    return send
+
+
+def ulysses_exchange(sends):
+    """The all-to-all itself, simulated: device dst receives piece dst of
+    every device's send buffer, in source order: recv[dst][src] = send[src][dst]."""
+    groups = len(sends)
+    return [np.stack([sends[src][dst] for src in range(groups)]) for dst in range(groups)]
+
+
+def ulysses_unpack(recv):
+    """recv [G, Nl, Hg, d] -> y [Nl, G*Hg, d] with y[i, g*Hg + j] = recv[g, i, j]."""
+    recv = np.asarray(recv)
+    groups, nl, hg, d = recv.shape
+    y = np.empty((nl, groups * hg, d), dtype=recv.dtype)
+    for g in range(groups):
+        y[:, g * hg:(g + 1) * hg, :] = recv[g]
+    return y
