@@ -31,6 +31,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-ring-split", action="store_true",
+                    help="skip the key-split + merge leg (profiling runs of the window alone)")
+    ap.add_argument("--ring-split-only", action="store_true",
+                    help="run only the key-split + merge leg and print it")
+    ap.add_argument("--no-ulysses", action="store_true",
+                    help="skip the Ulysses layout leg (profiling runs of the window alone)")
+    ap.add_argument("--ulysses-only", action="store_true",
+                    help="run only the Ulysses layout leg and print it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run 3 device-to-device copies of this many MiB (to scale HBM "
                          "byte counters against a copy of known size) and exit")
@@ -110,6 +118,117 @@ def cpu_baseline(w, target_s):
     }
 
 
+def ring_split(w, qkv, stream, reps=10):
+    """The one-GPU piece of a Ring split with R = 2: attention of all queries
+    over each key half (with log-sum-exp), then the exact merge, against one
+    call over all keys. Also the merge kernel alone, against HBM bandwidth."""
+    import torch
+
+    from diffusion_transformer_attention_dit_amd import native
+    q, k, v = qkv
+    half = w.tokens // 2
+    k1, v1 = k[:, :half].contiguous(), v[:, :half].contiguous()
+    k2, v2 = k[:, half:].contiguous(), v[:, half:].contiguous()
+    attn = native.Attention(w.heads, w.head_dim, w.grid)
+    o_full, l_full = torch.empty_like(q), torch.empty(w.heads, w.tokens, device=q.device)
+    o1, o2, o = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    l1, l2, lse = (torch.empty(w.heads, w.tokens, device=q.device) for _ in range(3))
+
+    def split():
+        attn.forward_range(q, 0, k1, v1, 0, out=o1, lse=l1, stream=stream)
+        attn.forward_range(q, 0, k2, v2, half, out=o2, lse=l2, stream=stream)
+        native.merge([o1, o2], [l1, l2], out=o, lse=lse, stream=stream)
+
+    def full():
+        attn.forward_range(q, 0, k, v, 0, out=o_full, lse=l_full, stream=stream)
+
+    def merge_only():
+        native.merge([o1, o2], [l1, l2], out=o, lse=lse, stream=stream)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_full, t_split, t_merge = timed(full), timed(split), timed(merge_only)
+    attn.close()
+    rows = w.heads * w.tokens
+    merge_bytes = 2 * (rows * w.head_dim * 2 + rows * 4) + rows * w.head_dim * 2 + rows * 4
+    gbs = merge_bytes / (t_merge * 1e-3) / 1e9
+    return {
+        "what": "all queries over key halves [0, %d) and [%d, %d) with lse, then the exact merge, "
+                "vs one call over all keys with lse" % (half, half, w.tokens),
+        "full_with_lse_ms": round(t_full, 4), "two_halves_and_merge_ms": round(t_split, 4),
+        "merge_kernel": {"kernel": "merge_parts_kernel", "avg_launch_us": round(t_merge * 1e3, 2),
+                         "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes": merge_bytes},
+    }
+
+
+def ulysses_leg(w, groups=4, reps=20):
+    """One device's share of Ulysses degree 4 at the window's shape: pack its
+    token shard of Q for the all-to-all, attention of its head group on the
+    exchanged token-major layout (against the head-major call), and unpack
+    of its O shard after the reverse exchange."""
+    import torch
+
+    from diffusion_transformer_attention_dit_amd import native, synth
+    N, H, d = w.tokens, w.heads, w.head_dim
+    nl, hg = N // groups, H // groups
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(77)
+    x = torch.randn(nl, H, d, generator=g, device="cuda").to(torch.bfloat16)
+    send = torch.empty(groups, nl, hg, d, dtype=torch.bfloat16, device="cuda")
+    back = torch.empty_like(x)
+    share = synth.WORKLOADS["ulysses_share_3x128_n10920"]
+    q, k, v = synth.make_qkv(share, device="cuda")
+    qt, kt, vt = (t.transpose(0, 1).contiguous() for t in (q, k, v))
+    o = torch.empty_like(q)
+    ot = torch.empty_like(qt)
+    a_hm = native.Attention(hg, d, w.grid)
+    a_tm = native.Attention(hg, d, w.grid, flags=native.REGEN_ATTN_TOKEN_MAJOR)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_pack = timed(lambda: native.ulysses_pack(x, groups, out=send, stream=stream))
+    t_unpack = timed(lambda: native.ulysses_unpack(send, out=back, stream=stream))
+    t_hm = timed(lambda: a_hm.forward(q, k, v, out=o, stream=stream))
+    t_tm = timed(lambda: a_tm.forward(qt, kt, vt, out=ot, stream=stream))
+    a_hm.close()
+    a_tm.close()
+    moved = 2 * nl * H * d * 2  # read + write of one shard
+
+    def leg(t_ms, kernel):
+        gbs = moved / (t_ms * 1e-3) / 1e9
+        return {"kernel": kernel, "avg_launch_us": round(t_ms * 1e3, 2), "bound": "hbm",
+                "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": moved}
+    return {
+        "what": "Ulysses degree %d at %d tokens x %d heads: pack of one %d-token shard, attention "
+                "of one %d-head group on the exchanged token-major layout vs head-major, unpack "
+                "of one shard" % (groups, N, H, nl, hg),
+        "pack": leg(t_pack, "block_transpose_kernel"),
+        "unpack": leg(t_unpack, "block_transpose_kernel"),
+        "attention_token_major_ms": round(t_tm, 4), "attention_head_major_ms": round(t_hm, 4),
+    }
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -139,6 +258,14 @@ def main():
     native.lib()  # fail loudly if the HIP library is missing
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.ulysses_only:
+        print(json.dumps({"workload": w.name, "ulysses": ulysses_leg(w)}), flush=True)
+        return 0
+    if args.ring_split_only:
+        qkv = synth.make_qkv(w, 0, 0, device="cuda")
+        print(json.dumps({"workload": w.name, "ring_split": ring_split(
+            w, qkv, torch.cuda.current_stream())}), flush=True)
+        return 0
     print("bench: drawing %d calls of %s" % (w.calls, w.name), file=sys.stderr, flush=True)
     drv = WindowDriver(w, device="cuda")
     # A second handle with kernel events, used for the per-kernel timing of
@@ -224,6 +351,10 @@ def main():
         },
         "merge_kernel": {"kernel": "merge_kernel", "avg_launch_us": round(merge_avg_s * 1e6, 2)},
     }
+    if not args.no_ring_split:
+        line["ring_split"] = ring_split(w, drv.inputs[0], stream)
+    if not args.no_ulysses:
+        line["ulysses"] = ulysses_leg(w)
     drv.close()
     del drv
     torch.cuda.empty_cache()

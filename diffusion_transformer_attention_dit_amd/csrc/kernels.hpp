@@ -100,6 +100,9 @@ __device__ __forceinline__ uint4 rope_chunk(uint4 in, const float2* __restrict__
 
 // ---------------------------------------------------------------------------
 // Kernel 1: K rotation + V transpose. Grid (Npad / 128, heads), 256 threads.
+//   k, v : bf16, key n of head h at element h * sh + n * sn (head-major
+//          [heads][N][D]: sh = N D, sn = D; token-major [N][heads][D]:
+//          sh = D, sn = heads D), key n being token n_off + n of the grid.
 //   Kr : [heads][Npad][D] bf16, rotated, rows >= N zero.
 //   Vt : [heads][Npad/64][D][64] bf16; inside each group of 16 slots, slot
 //        8g + j holds key 8(j/4) + 4g + j%4 of that group; keys >= N zero.
@@ -107,7 +110,8 @@ __device__ __forceinline__ uint4 rope_chunk(uint4 in, const float2* __restrict__
 template <int D>
 __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ kr,
-    uint16_t* __restrict__ vt, const float2* __restrict__ tab, RopeGeom geo, int N, int Npad) {
+    uint16_t* __restrict__ vt, const float2* __restrict__ tab, RopeGeom geo, int N, int Npad,
+    int n_off, long long sh, long long sn) {
     constexpr int CPR = D / 8;  // 16-byte chunks per row
     const int tile = blockIdx.x, hd = blockIdx.y;
     const int n0 = tile * kPrepKeys;
@@ -118,8 +122,9 @@ __global__ __launch_bounds__(256) void rope_k_vt_kernel(
         const int n = n0 + r;
         uint4 out = make_uint4(0, 0, 0, 0);
         if (n < N) {
-            uint4 in = *reinterpret_cast<const uint4*>(k + ((size_t)hd * N + n) * D + c * 8);
-            const int t = n / HW, h = (n / geo.W) % geo.H, w = n % geo.W;
+            uint4 in = *reinterpret_cast<const uint4*>(k + hd * sh + n * sn + c * 8);
+            const int ng = n_off + n;  // token index on the grid
+            const int t = ng / HW, h = (ng / geo.W) % geo.H, w = ng % geo.W;
             out = rope_chunk(in, tab, geo, c * 4, t, h, w);
         }
         *reinterpret_cast<uint4*>(kr + ((size_t)hd * Npad + n) * D + c * 8) = out;
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(256) void rope_k_vt_kernel(
         for (int j = 0; j < 8; ++j) {
             const int key = n0 + G * 16 + (j / 4) * 8 + hh * 4 + (j % 4);
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (key < N) x = *reinterpret_cast<const uint4*>(v + ((size_t)hd * N + key) * D + c * 8);
+            if (key < N) x = *reinterpret_cast<const uint4*>(v + hd * sh + key * sn + c * 8);
             a[j][0] = x.x; a[j][1] = x.y; a[j][2] = x.z; a[j][3] = x.w;
         }
         uint16_t* dst = vt + ((size_t)(hd * (Npad / kVtBlk) + tile * 2 + blk) * D + c * 8) * kVtBlk + g * 8;
@@ -284,14 +289,19 @@ __device__ __forceinline__ bool get_segment(const Sched& sc, int p, int k, long 
 
 // ---------------------------------------------------------------------------
 // Kernel 2: attention, persistent. Grid P, NW * 64 threads.
+//   q, o    : bf16, row m of head h at element h * qh + m * qn (head-major or
+//             token-major as for kernel 1), row m being token q_off + m
+//   Kr, Vt  : the Nk keys prepared by kernel 1 (Npad rows per head)
+//   lse     : [heads][Nq] fp32 log-sum-exp of each row's scores, or null
 //   part_o  : [2P][BM][D] fp32 unnormalised O of split tiles
 //   part_ml : [2P][BM][2] fp32 (m, l) of split tiles
 // ---------------------------------------------------------------------------
 template <int D, int BN, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kr,
-    const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, const float2* __restrict__ tab,
-    RopeGeom geo, int N, int Npad, Sched sc, float c2 /* sm_scale * log2(e) */,
+    const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, float* __restrict__ lse,
+    const float2* __restrict__ tab, RopeGeom geo, int Nq, int Nk, int Npad, int q_off,
+    long long qh, long long qn_stride, Sched sc, float c2 /* sm_scale * log2(e) */,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(BN == 64 || BN == 128, "key tile");
@@ -343,13 +353,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // exp2 domain.
         bf16x8 qf[D / 16];
         {
-            const int qn = qrow < N ? qrow : 0;
-            const int tt = qn / HW, hh = (qn / geo.W) % geo.H, ww = qn % geo.W;
-            const uint16_t* qp = q + ((size_t)hd * N + qn) * D + half * 8;
+            const int qn = qrow < Nq ? qrow : 0;
+            const int qg = q_off + qn;  // token index on the grid
+            const int tt = qg / HW, hh = (qg / geo.W) % geo.H, ww = qg % geo.W;
+            const uint16_t* qp = q + hd * qh + qn * qn_stride + half * 8;
 #pragma unroll
             for (int kb = 0; kb < D / 16; ++kb) {
                 uint4 x = make_uint4(0, 0, 0, 0);
-                if (qrow < N) {
+                if (qrow < Nq) {
                     x = *reinterpret_cast<const uint4*>(qp + kb * 16);
                     x = rope_chunk(x, tab, geo, kb * 8 + half * 4, tt, hh, ww, c2);
                 }
@@ -427,13 +438,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
             __builtin_amdgcn_s_setprio(0);
             // Keys past the end of the sequence get -inf (never zero-padding).
-            if (b == sc.nkv - 1 && (N % BN) != 0) {
+            if (b == sc.nkv - 1 && (Nk % BN) != 0) {
 #pragma unroll
                 for (int kk = 0; kk < BN / 32; ++kk)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int key = b * BN + kk * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-                        if (key >= N) s[kk][i] = -INFINITY;
+                        if (key >= Nk) s[kk][i] = -INFINITY;
                     }
             }
 
@@ -518,10 +529,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                                    false, false);
         const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         if (kv0 == 0 && kv1 == sc.nkv) {
-            // Whole tile here: O = O^T / l, bf16.
+            // Whole tile here: O = O^T / l, bf16; lse = ln 2 (m + log2 l).
             const float inv = 1.0f / l_row;
-            if (qrow < N) {
-                uint16_t* op = o + ((size_t)hd * N + qrow) * D;
+            if (qrow < Nq) {
+                if (lse != nullptr && half == 0)
+                    lse[(size_t)hd * Nq + qrow] = (m_run + log2f(l_row)) * 0.69314718055994531f;
+                uint16_t* op = o + hd * qh + qrow * qn_stride;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -567,10 +580,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // through LDS the same way.
 // ---------------------------------------------------------------------------
 template <int D, int NW>
-__global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o,
+__global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, float* __restrict__ lse,
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml, int N,
-                                                    Sched sc) {
+                                                    Sched sc, long long qh, long long qn_stride) {
     constexpr int BM = NW * 32;
     constexpr int DPT = D / 32;  // head dims per thread (4 or 2)
     const long long t = (long long)sc.full * sc.P + blockIdx.x;
@@ -624,7 +637,8 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o,
         for (int i = 0; i < DPT; ++i) out[i] += w * sm[k][g][2 + i];
     }
     const float inv = 1.0f / L;
-    uint16_t* op = o + ((size_t)hd * N + qrow) * D + d0;
+    if (lse != nullptr && g == 0) lse[(size_t)hd * N + qrow] = (M + log2f(L)) * 0.69314718055994531f;
+    uint16_t* op = o + hd * qh + qrow * qn_stride + d0;
     if constexpr (DPT == 4) {
         uint2 w2;
         w2.x = pack_bf16(out[0] * inv, out[1] * inv);
@@ -633,6 +647,85 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o,
     } else {
         *reinterpret_cast<uint32_t*>(op) = pack_bf16(out[0] * inv, out[1] * inv);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 4: combine attention results over disjoint key sets (Ring-style key
+// splitting keeps attention exact this way). Part i holds O_i [rows][D] bf16,
+// normalised over its own keys, and lse_i [rows] fp32; over the union of the
+// key sets
+//     lse = log sum_i e^{lse_i},   O = sum_i e^{lse_i - lse} O_i.
+// D/8 lanes per row (8 head dims, 16 bytes each), 256 threads per block. A
+// row whose parts are all -inf (no keys anywhere) gets O = 0, lse = -inf.
+// ---------------------------------------------------------------------------
+constexpr int kMaxMergeParts = 8;
+struct MergeParts {
+    const uint16_t* o[kMaxMergeParts];
+    const float* lse[kMaxMergeParts];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_parts_kernel(MergeParts parts, int nparts,
+                                                          long long rows,
+                                                          uint16_t* __restrict__ o,
+                                                          float* __restrict__ lse) {
+    constexpr int LPR = D / 8;  // lanes per row
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long row = gid / LPR;
+    const int c = (int)(gid % LPR);
+    if (row >= rows) return;
+    constexpr float kLog2e = 1.4426950408889634f;
+    float li[kMaxMergeParts];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMaxMergeParts; ++i) {
+        li[i] = (i < nparts) ? parts.lse[i][row] : -INFINITY;
+        m = fmaxf(m, li[i]);
+    }
+    uint16_t* op = o + row * D + c * 8;
+    if (m == -INFINITY) {
+        *reinterpret_cast<uint4*>(op) = make_uint4(0, 0, 0, 0);
+        if (lse != nullptr && c == 0) lse[row] = -INFINITY;
+        return;
+    }
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxMergeParts; ++i) {
+        if (i >= nparts) break;
+        const float w = __builtin_amdgcn_exp2f((li[i] - m) * kLog2e);
+        z += w;
+        const uint4 x = *reinterpret_cast<const uint4*>(parts.o[i] + row * D + c * 8);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += w * bf_lo(xs[e]);
+            acc[2 * e + 1] += w * bf_hi(xs[e]);
+        }
+    }
+    const float inv = 1.0f / z;
+    *reinterpret_cast<uint4*>(op) =
+        make_uint4(pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv),
+                   pack_bf16(acc[4] * inv, acc[5] * inv), pack_bf16(acc[6] * inv, acc[7] * inv));
+    if (lse != nullptr && c == 0) lse[row] = m + logf(z);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 5: the on-device half of a Ulysses all-to-all (blog summary,
+// "Methodology - deep read", USP paragraph: Ulysses turns sequence shards
+// into head shards). A block transpose src [A][B][E] -> dst [B][A][E] of
+// E-byte blocks, 16 bytes per thread, writes in destination order:
+//   pack   [Nl][G][H/G][D] -> [G][Nl][H/G][D]  (A = Nl, B = G)
+//   unpack [G][Nl][H/G][D] -> [Nl][G][H/G][D]  (A = G, B = Nl)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void block_transpose_kernel(const uint4* __restrict__ src,
+                                                              uint4* __restrict__ dst, long long A,
+                                                              long long B, long long E16) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= A * B * E16) return;
+    const long long e = i % E16, ba = i / E16;
+    const long long a = ba % A, b = ba / A;
+    dst[i] = src[(a * B + b) * E16 + e];
 }
 
 }  // namespace regen

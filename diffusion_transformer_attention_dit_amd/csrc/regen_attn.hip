@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr uint32_t kKnownFlags = REGEN_ATTN_NO_ROPE | REGEN_ATTN_PROFILE;
+constexpr uint32_t kKnownFlags = REGEN_ATTN_NO_ROPE | REGEN_ATTN_PROFILE | REGEN_ATTN_TOKEN_MAJOR;
 // Attention kernel shape: NW waves of 32 query rows, BN-key blocks.
 constexpr int kNW = 8, kBM = kNW * 32, kBN = 64;
 constexpr int64_t kMaxTokens = int64_t(1) << 30;
@@ -269,19 +269,43 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
     return REGEN_OK;
 }
 
-regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, const void* v,
-                                void* o, void* stream) {
-    g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// Overlap test of two byte ranges [a, a + na) and [b, b + nb).
+bool overlaps(uintptr_t a, uintptr_t na, uintptr_t b, uintptr_t nb) {
+    return a < b + nb && b < a + na;
+}
+
+// One attention call: query tokens [q_begin, q_begin + nq) against key
+// tokens [kv_begin, kv_begin + nk) of the handle's window.
+regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, const void* k,
+                    const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse,
+                    void* stream) {
     if (!h || !is_live(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is NULL or not live");
     if (!q || !k || !v || !o) return fail(REGEN_ERR_INVALID_ARGUMENT, "q, k, v, o must be non-NULL");
+    const Problem& p = h->p;
+    if (q_begin < 0 || nq < 1 || q_begin + nq > p.tokens)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "query range outside [0, grid_t*grid_h*grid_w)");
+    if (kv_begin < 0 || nk < 1 || kv_begin + nk > p.tokens)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "key range outside [0, grid_t*grid_h*grid_w)");
     const uintptr_t ptrs[4] = {uintptr_t(q), uintptr_t(k), uintptr_t(v), uintptr_t(o)};
     for (uintptr_t a : ptrs)
         if (a % 16 != 0) return fail(REGEN_ERR_INVALID_ARGUMENT, "q, k, v, o must be 16-byte aligned");
-    const Problem& p = h->p;
-    const uintptr_t bytes = uintptr_t(p.heads) * uintptr_t(p.tokens) * uintptr_t(p.head_dim) * 2;
-    for (int i = 0; i < 3; ++i)
-        if (ptrs[3] < ptrs[i] + bytes && ptrs[i] < ptrs[3] + bytes)
-            return fail(REGEN_ERR_INVALID_ARGUMENT, "o overlaps q, k or v");
+    if (lse && uintptr_t(lse) % 4 != 0)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+    const uintptr_t row = uintptr_t(p.heads) * uintptr_t(p.head_dim) * 2;
+    const uintptr_t qbytes = row * uintptr_t(nq), kbytes = row * uintptr_t(nk);
+    const uintptr_t lbytes = uintptr_t(p.heads) * uintptr_t(nq) * 4;
+    if (overlaps(ptrs[3], qbytes, ptrs[0], qbytes) || overlaps(ptrs[3], qbytes, ptrs[1], kbytes) ||
+        overlaps(ptrs[3], qbytes, ptrs[2], kbytes))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "o overlaps q, k or v");
+    if (lse && (overlaps(uintptr_t(lse), lbytes, ptrs[0], qbytes) ||
+                overlaps(uintptr_t(lse), lbytes, ptrs[1], kbytes) ||
+                overlaps(uintptr_t(lse), lbytes, ptrs[2], kbytes) ||
+                overlaps(uintptr_t(lse), lbytes, ptrs[3], qbytes)))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "lse overlaps q, k, v or o");
 
     int cur = -1;
     hipError_t ge = hipGetDevice(&cur);
@@ -290,23 +314,30 @@ regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, co
         return fail(REGEN_ERR_INVALID_ARGUMENT, "the current HIP device is not the handle's device");
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int N = int(p.tokens), Npad = int(p.tokens_pad);
+    const int Nq = int(nq), Nk = int(nk);
+    const int Npad = int((nk + regen::kPrepKeys - 1) / regen::kPrepKeys * regen::kPrepKeys);
     const float c2 = p.scale * 1.4426950408889634f;
 
     dim3 pgrid(unsigned(Npad / regen::kPrepKeys), unsigned(p.heads));
-    const int64_t tiles = int64_t(p.heads) * p.n_qtiles;
     regen::Sched sc;
-    sc.n_qtiles = p.n_qtiles;
-    sc.nkv = p.nkv;
+    sc.n_qtiles = int((nq + kBM - 1) / kBM);
+    sc.nkv = int((nk + kBN - 1) / kBN);
+    const int64_t tiles = int64_t(p.heads) * sc.n_qtiles;
     sc.P = h->P;
     sc.full = int(tiles / h->P);
     const int64_t rem_tiles = tiles - int64_t(sc.full) * h->P;
-    sc.rem_units = rem_tiles * p.nkv;
+    sc.rem_units = rem_tiles * sc.nkv;
     const dim3 mgrid{unsigned(rem_tiles), unsigned(kBM), 1u};
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
     const uint16_t* k16 = static_cast<const uint16_t*>(k);
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
     uint16_t* o16 = static_cast<uint16_t*>(o);
+    const int q_off = int(q_begin), k_off = int(kv_begin);
+    // Element strides of (head, token) in q/o and in k/v.
+    const bool tm = (p.flags & REGEN_ATTN_TOKEN_MAJOR) != 0;
+    const long long D = p.head_dim;
+    const long long qh = tm ? D : nq * D, qn = tm ? p.heads * D : D;
+    const long long kh = tm ? D : nk * D, kn = tm ? p.heads * D : D;
 
     ProfRecord rec{};
     const bool prof = (p.flags & REGEN_ATTN_PROFILE) != 0;
@@ -331,26 +362,26 @@ regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, co
 
     if (p.head_dim == 128) {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<128>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
-                           h->d_vt, h->d_tab, h->geo, N, Npad);
+                           h->d_vt, h->d_tab, h->geo, Nk, Npad, k_off, kh, kn);
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<128, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
-                           st, q16, h->d_kr, h->d_vt, o16, h->d_tab, h->geo, N, Npad, sc, c2,
-                           h->d_part_o, h->d_part_ml);
+                           st, q16, h->d_kr, h->d_vt, o16, lse, h->d_tab, h->geo, Nq, Nk, Npad,
+                           q_off, qh, qn, sc, c2, h->d_part_o, h->d_part_ml);
         mark(2);
         if (rem_tiles > 0)
-            hipLaunchKernelGGL((regen::merge_kernel<128, kNW>), mgrid, dim3(256), 0, st, o16,
-                               h->d_part_o, h->d_part_ml, N, sc);
+            hipLaunchKernelGGL((regen::merge_kernel<128, kNW>), mgrid, dim3(256), 0, st, o16, lse,
+                               h->d_part_o, h->d_part_ml, Nq, sc, qh, qn);
     } else {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
-                           h->d_vt, h->d_tab, h->geo, N, Npad);
+                           h->d_vt, h->d_tab, h->geo, Nk, Npad, k_off, kh, kn);
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<64, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
-                           st, q16, h->d_kr, h->d_vt, o16, h->d_tab, h->geo, N, Npad, sc, c2,
-                           h->d_part_o, h->d_part_ml);
+                           st, q16, h->d_kr, h->d_vt, o16, lse, h->d_tab, h->geo, Nq, Nk, Npad,
+                           q_off, qh, qn, sc, c2, h->d_part_o, h->d_part_ml);
         mark(2);
         if (rem_tiles > 0)
-            hipLaunchKernelGGL((regen::merge_kernel<64, kNW>), mgrid, dim3(256), 0, st, o16,
-                               h->d_part_o, h->d_part_ml, N, sc);
+            hipLaunchKernelGGL((regen::merge_kernel<64, kNW>), mgrid, dim3(256), 0, st, o16, lse,
+                               h->d_part_o, h->d_part_ml, Nq, sc, qh, qn);
     }
     hipError_t e = hipGetLastError();
     if (prof) {
@@ -359,6 +390,142 @@ regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, co
     }
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     return REGEN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+regen_status regen_attn_forward(regen_attn_t h, const void* q, const void* k, const void* v,
+                                void* o, void* stream) {
+    g_last_error.clear();
+    if (!h || !is_live(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is NULL or not live");
+    return launch(h, q, 0, h->p.tokens, k, v, 0, h->p.tokens, o, nullptr, stream);
+}
+
+regen_status regen_attn_forward_range(regen_attn_t h, const void* q, int64_t q_begin,
+                                      int64_t q_count, const void* k, const void* v,
+                                      int64_t kv_begin, int64_t kv_count, void* o, float* lse,
+                                      void* stream) {
+    g_last_error.clear();
+    return launch(h, q, q_begin, q_count, k, v, kv_begin, kv_count, o, lse, stream);
+}
+
+regen_status regen_attn_merge(const void* const* o_parts, const float* const* lse_parts,
+                              int nparts, int heads, int64_t rows, int head_dim, void* o,
+                              float* lse, void* stream) {
+    g_last_error.clear();
+    if (!o_parts || !lse_parts || !o)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "o_parts, lse_parts and o must be non-NULL");
+    if (nparts < 1 || nparts > regen::kMaxMergeParts)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "nparts must be in [1, 8]");
+    if (heads < 1 || rows < 1) return fail(REGEN_ERR_INVALID_ARGUMENT, "heads and rows must be >= 1");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(REGEN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    const int64_t total = int64_t(heads) * rows;
+    if (total > (int64_t(1) << 40) / head_dim)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "tensor too large");
+    const uintptr_t obytes = uintptr_t(total) * uintptr_t(head_dim) * 2;
+    const uintptr_t lbytes = uintptr_t(total) * 4;
+    if (uintptr_t(o) % 16 != 0 || (lse && uintptr_t(lse) % 4 != 0))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "o must be 16-byte and lse 4-byte aligned");
+    regen::MergeParts mp{};
+    for (int i = 0; i < nparts; ++i) {
+        if (!o_parts[i] || !lse_parts[i])
+            return fail(REGEN_ERR_INVALID_ARGUMENT, "a part pointer is NULL");
+        if (uintptr_t(o_parts[i]) % 16 != 0 || uintptr_t(lse_parts[i]) % 4 != 0)
+            return fail(REGEN_ERR_INVALID_ARGUMENT, "o parts must be 16-byte and lse parts 4-byte aligned");
+        if (overlaps(uintptr_t(o), obytes, uintptr_t(o_parts[i]), obytes) ||
+            overlaps(uintptr_t(o), obytes, uintptr_t(lse_parts[i]), lbytes) ||
+            (lse && (overlaps(uintptr_t(lse), lbytes, uintptr_t(o_parts[i]), obytes) ||
+                     overlaps(uintptr_t(lse), lbytes, uintptr_t(lse_parts[i]), lbytes))))
+            return fail(REGEN_ERR_INVALID_ARGUMENT, "an output overlaps an input part");
+        mp.o[i] = static_cast<const uint16_t*>(o_parts[i]);
+        mp.lse[i] = lse_parts[i];
+    }
+    if (lse && overlaps(uintptr_t(lse), lbytes, uintptr_t(o), obytes))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "lse overlaps o");
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count < 1) {
+        (void)hipGetLastError();
+        return fail(REGEN_ERR_NO_DEVICE, "no HIP device is available");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t threads = total * (head_dim / 8);
+    const dim3 grid{unsigned((threads + 255) / 256), 1u, 1u};
+    if (head_dim == 128)
+        hipLaunchKernelGGL(regen::merge_parts_kernel<128>, grid, dim3(256), 0, st, mp, nparts,
+                           (long long)total, static_cast<uint16_t*>(o), lse);
+    else
+        hipLaunchKernelGGL(regen::merge_parts_kernel<64>, grid, dim3(256), 0, st, mp, nparts,
+                           (long long)total, static_cast<uint16_t*>(o), lse);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    return REGEN_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// dst [B][A][E] <- src [A][B][E], E = bytes per block (a multiple of 16).
+regen_status block_transpose(const void* src, void* dst, int64_t A, int64_t B, int64_t E,
+                             void* stream) {
+    if (!src || !dst) return fail(REGEN_ERR_INVALID_ARGUMENT, "src and dst must be non-NULL");
+    if (uintptr_t(src) % 16 != 0 || uintptr_t(dst) % 16 != 0)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+    const int64_t bytes = A * B * E;
+    if (overlaps(uintptr_t(src), uintptr_t(bytes), uintptr_t(dst), uintptr_t(bytes)))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "dst overlaps src");
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count < 1) {
+        (void)hipGetLastError();
+        return fail(REGEN_ERR_NO_DEVICE, "no HIP device is available");
+    }
+    const int64_t n16 = bytes / 16;
+    const dim3 grid{unsigned((n16 + 255) / 256), 1u, 1u};
+    hipLaunchKernelGGL(regen::block_transpose_kernel, grid, dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
+                       static_cast<uint4*>(dst), (long long)A, (long long)B, (long long)(E / 16));
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    return REGEN_OK;
+}
+
+regen_status ulysses_shape(int64_t tokens_local, int heads, int head_dim, int groups, int64_t* E) {
+    if (tokens_local < 1 || heads < 1 || groups < 1 || head_dim < 1)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "tokens_local, heads, head_dim, groups must be >= 1");
+    if (heads % groups != 0) return fail(REGEN_ERR_INVALID_ARGUMENT, "heads must be a multiple of groups");
+    if ((int64_t(heads / groups) * head_dim * 2) % 16 != 0)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "(heads/groups) * head_dim * 2 must be a multiple of 16");
+    if (tokens_local * heads * int64_t(head_dim) > (int64_t(1) << 40))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "tensor too large");
+    *E = int64_t(heads / groups) * head_dim * 2;
+    return REGEN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+regen_status regen_ulysses_pack(const void* x, void* send, int64_t tokens_local, int heads,
+                                int head_dim, int groups, void* stream) {
+    g_last_error.clear();
+    int64_t E = 0;
+    regen_status s = ulysses_shape(tokens_local, heads, head_dim, groups, &E);
+    if (s != REGEN_OK) return s;
+    return block_transpose(x, send, tokens_local, groups, E, stream);
+}
+
+regen_status regen_ulysses_unpack(const void* recv, void* y, int64_t tokens_local, int heads,
+                                  int head_dim, int groups, void* stream) {
+    g_last_error.clear();
+    int64_t E = 0;
+    regen_status s = ulysses_shape(tokens_local, heads, head_dim, groups, &E);
+    if (s != REGEN_OK) return s;
+    return block_transpose(recv, y, groups, tokens_local, E, stream);
 }
 
 regen_status regen_attn_profile_read(regen_attn_t h, double* prep_ms, double* attn_ms,

@@ -18,11 +18,16 @@ REGEN_ERR_HIP = 5
 
 REGEN_ATTN_NO_ROPE = 0x1
 REGEN_ATTN_PROFILE = 0x2
+REGEN_ATTN_TOKEN_MAJOR = 0x4
 
 # Names the header declares; the CPU tests check the library exports each.
 EXPORTS = (
     "regen_attn_create",
     "regen_attn_forward",
+    "regen_attn_forward_range",
+    "regen_attn_merge",
+    "regen_ulysses_pack",
+    "regen_ulysses_unpack",
     "regen_attn_destroy",
     "regen_attn_status_string",
     "regen_attn_last_error",
@@ -76,6 +81,16 @@ def lib():
     L.regen_attn_create.restype = ctypes.c_int
     L.regen_attn_forward.argtypes = [vp, vp, vp, vp, vp, vp]
     L.regen_attn_forward.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    L.regen_attn_forward_range.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, vp, vp, vp]
+    L.regen_attn_forward_range.restype = ctypes.c_int
+    L.regen_attn_merge.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int,
+                                   ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
+    L.regen_attn_merge.restype = ctypes.c_int
+    for name in ("regen_ulysses_pack", "regen_ulysses_unpack"):
+        f = getattr(L, name)
+        f.argtypes = [vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+        f.restype = ctypes.c_int
     L.regen_attn_destroy.argtypes = [vp]
     L.regen_attn_destroy.restype = ctypes.c_int
     L.regen_attn_status_string.argtypes = [ctypes.c_int]
@@ -114,6 +129,32 @@ def regen_attn_forward(handle, q, k, v, o, stream):
     return lib().regen_attn_forward(handle, q, k, v, o, stream)
 
 
+def regen_attn_forward_range(handle, q, q_begin, q_count, k, v, kv_begin, kv_count, o, lse,
+                             stream):
+    """Pointers are integer device addresses (lse may be 0 / None)."""
+    return lib().regen_attn_forward_range(handle, q, q_begin, q_count, k, v, kv_begin, kv_count,
+                                          o, lse or None, stream)
+
+
+def regen_attn_merge(o_parts, lse_parts, heads, rows, head_dim, o, lse, stream):
+    """o_parts, lse_parts: sequences of integer device addresses."""
+    n = len(o_parts)
+    vp = ctypes.c_void_p
+    op = (vp * max(n, 1))(*[vp(a) for a in o_parts])
+    lp = (vp * max(len(lse_parts), 1))(*[vp(a) for a in lse_parts])
+    return lib().regen_attn_merge(op if o_parts is not None else None,
+                                  lp if lse_parts is not None else None, n, heads, rows,
+                                  head_dim, o, lse or None, stream)
+
+
+def regen_ulysses_pack(x, send, tokens_local, heads, head_dim, groups, stream):
+    return lib().regen_ulysses_pack(x, send, tokens_local, heads, head_dim, groups, stream)
+
+
+def regen_ulysses_unpack(recv, y, tokens_local, heads, head_dim, groups, stream):
+    return lib().regen_ulysses_unpack(recv, y, tokens_local, heads, head_dim, groups, stream)
+
+
 def regen_attn_destroy(handle):
     return lib().regen_attn_destroy(handle)
 
@@ -138,7 +179,67 @@ def regen_attn_profile_read(handle):
     return s, a.value, b.value, c.value, n.value
 
 
-# ---- a small convenience wrapper over torch tensors ------------------------
+# ---- small convenience wrappers over torch tensors --------------------------
+
+def ulysses_pack(x, groups, out=None, stream=None):
+    """x [tokens_local, heads, d] bf16 -> [groups, tokens_local, heads/groups, d]."""
+    import torch
+    nl, heads, d = (int(a) for a in x.shape)
+    if out is None:
+        out = torch.empty((groups, nl, heads // groups, d), dtype=x.dtype, device=x.device)
+    _ulysses_call(regen_ulysses_pack, x, out, nl, heads, d, groups, stream, "regen_ulysses_pack")
+    return out
+
+
+def ulysses_unpack(recv, out=None, stream=None):
+    """recv [groups, tokens_local, heads/groups, d] bf16 -> [tokens_local, heads, d]."""
+    import torch
+    groups, nl, hg, d = (int(a) for a in recv.shape)
+    if out is None:
+        out = torch.empty((nl, groups * hg, d), dtype=recv.dtype, device=recv.device)
+    _ulysses_call(regen_ulysses_unpack, recv, out, nl, groups * hg, d, groups, stream,
+                  "regen_ulysses_unpack")
+    return out
+
+
+def _ulysses_call(fn, src, dst, nl, heads, d, groups, stream, name):
+    import torch
+    for t in (src, dst):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("%s: tensors must be contiguous bf16 device tensors" % name)
+    if src.numel() != nl * heads * d or dst.numel() != src.numel():
+        raise ValueError("%s: sizes do not match" % name)
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device)
+    s = fn(src.data_ptr(), dst.data_ptr(), nl, heads, d, groups, stream.cuda_stream)
+    if s != REGEN_OK:
+        raise RegenAttnError(s, name)
+
+def merge(o_parts, lse_parts, out=None, lse=None, stream=None):
+    """Combine results over disjoint key sets: o_parts bf16 [heads, rows, d],
+    lse_parts fp32 [heads, rows] (torch device tensors). Returns (o, lse)."""
+    import torch
+    if len(o_parts) != len(lse_parts) or not o_parts:
+        raise ValueError("need as many lse parts as o parts, at least one")
+    heads, rows, d = (int(x) for x in o_parts[0].shape)
+    for o_, l_ in zip(o_parts, lse_parts):
+        if o_.dtype != torch.bfloat16 or not o_.is_contiguous() or tuple(o_.shape) != (heads, rows, d):
+            raise ValueError("o parts must be contiguous bf16 [heads, rows, d] tensors of one shape")
+        if l_.dtype != torch.float32 or not l_.is_contiguous() or tuple(l_.shape) != (heads, rows):
+            raise ValueError("lse parts must be contiguous fp32 [heads, rows] tensors")
+    if out is None:
+        out = torch.empty_like(o_parts[0])
+    if lse is None:
+        lse = torch.empty_like(lse_parts[0])
+    if stream is None:
+        stream = torch.cuda.current_stream(o_parts[0].device)
+    s = regen_attn_merge([t.data_ptr() for t in o_parts], [t.data_ptr() for t in lse_parts],
+                         heads, rows, d, out.data_ptr(), lse.data_ptr() if lse is not False else None,
+                         stream.cuda_stream)
+    if s != REGEN_OK:
+        raise RegenAttnError(s, "regen_attn_merge")
+    return out, (lse if lse is not False else None)
+
 
 class Attention:
     """One problem shape on the current device. torch supplies memory and the
@@ -154,9 +255,14 @@ class Attention:
             raise RegenAttnError(s, "regen_attn_create")
         self.handle = h
 
+    def _shape(self, n):
+        if self.desc.flags & REGEN_ATTN_TOKEN_MAJOR:
+            return (n, self.heads, self.head_dim)
+        return (self.heads, n, self.head_dim)
+
     def _check(self, t, name):
         import torch
-        shape = (self.heads, self.tokens, self.head_dim)
+        shape = self._shape(self.tokens)
         if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError("%s must be a contiguous bf16 device tensor" % name)
         if tuple(t.shape) != shape:
@@ -178,6 +284,41 @@ class Attention:
         return out
 
     __call__ = forward
+
+    def forward_range(self, q, q_begin, k, v, kv_begin, out=None, lse=None, stream=None):
+        """Query tokens q_begin.. (q: [heads, nq, d]) against key tokens
+        kv_begin.. (k, v: [heads, nk, d]). Returns (o, lse); lse=False skips
+        the log-sum-exp."""
+        import torch
+        tm = bool(self.desc.flags & REGEN_ATTN_TOKEN_MAJOR)
+        nq, nk = (int(q.shape[0]), int(k.shape[0])) if tm else (int(q.shape[1]), int(k.shape[1]))
+        for t, n, name in ((q, nq, "q"), (k, nk, "k"), (v, nk, "v")):
+            self._check_rows(t, n, name)
+        if out is None:
+            out = torch.empty_like(q)
+        self._check_rows(out, nq, "out")
+        if lse is None:
+            lse = torch.empty((self.heads, nq), dtype=torch.float32, device=q.device)
+        if lse is not False:
+            if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (self.heads, nq):
+                raise ValueError("lse must be a contiguous fp32 [heads, q_count] tensor")
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        s = regen_attn_forward_range(self.handle, q.data_ptr(), int(q_begin), nq, k.data_ptr(),
+                                     v.data_ptr(), int(kv_begin), nk, out.data_ptr(),
+                                     lse.data_ptr() if lse is not False else None,
+                                     stream.cuda_stream)
+        if s != REGEN_OK:
+            raise RegenAttnError(s, "regen_attn_forward_range")
+        return out, (lse if lse is not False else None)
+
+    def _check_rows(self, t, n, name):
+        import torch
+        shape = self._shape(n)
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous bf16 device tensor" % name)
+        if tuple(t.shape) != shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
 
     def profile_read(self):
         """(prep_ms, attn_ms, merge_ms, calls) since the last read; needs REGEN_ATTN_PROFILE."""

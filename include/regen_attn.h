@@ -29,7 +29,10 @@
  * (round-to-nearest-even throughout).
  *
  * Layout: q, k, v, o are contiguous bf16 tensors [heads][T*H*W][head_dim]
- * in device memory, 16-byte aligned, owned by the caller.
+ * in device memory, 16-byte aligned, owned by the caller; with the flag
+ * REGEN_ATTN_TOKEN_MAJOR they are [T*H*W][heads][head_dim] instead, the
+ * layout a Ulysses all-to-all delivers and expects back (see
+ * regen_ulysses_pack).
  *
  * Threading: a handle is bound to the HIP device that was current at
  * create. It owns a device workspace (rotated K and a transposed V), so calls
@@ -59,6 +62,8 @@ typedef enum regen_status {
 #define REGEN_ATTN_NO_ROPE 0x1u /* skip the rotation (plain exact attention) */
 #define REGEN_ATTN_PROFILE 0x2u /* record HIP events around each kernel (see
                                    regen_attn_profile_read) */
+#define REGEN_ATTN_TOKEN_MAJOR 0x4u /* q, k, v, o are [tokens][heads][head_dim]
+                                       (lse stays [heads][tokens]) */
 
 /*
  * Problem description. Zero in an optional field selects its default.
@@ -123,6 +128,83 @@ regen_status regen_attn_create(const regen_attn_desc *desc, regen_attn_t *out);
  */
 regen_status regen_attn_forward(regen_attn_t h, const void *q, const void *k,
                                 const void *v, void *o, void *stream);
+
+/*
+ * Attention of a run of query tokens against a run of key tokens of the
+ * handle's window, with the log-sum-exp of every row's scores. This is the
+ * piece of Ring-style sequence parallelism that one GPU computes (blog
+ * summary, "Methodology - deep read", USP paragraph: Ring circulates key and
+ * value blocks while each device keeps its queries; "Technical innovations":
+ * the split attention stays exact): results over separate key runs combine
+ * exactly with regen_attn_merge.
+ *   q     : [heads][q_count][head_dim] bf16, row m = token q_begin + m
+ *   k, v  : [heads][kv_count][head_dim] bf16, row n = token kv_begin + n
+ *   o     : [heads][q_count][head_dim] bf16, attention over those keys only
+ *   lse   : [heads][q_count] fp32, lse_m = log sum_n exp(sm_scale <R(m)q_m,
+ *           R(n)k_n>) (natural log), or NULL to skip it
+ * Each token is rotated at its own place on the latent grid (token index as
+ * in the file comment). Ranges must satisfy 0 <= begin, 1 <= count,
+ * begin + count <= grid_t*grid_h*grid_w. Pointers: device memory, o 16-byte
+ * aligned and not overlapping q, k, v; lse 4-byte aligned and not
+ * overlapping any other buffer. The same ordering rule as regen_attn_forward
+ * applies (the handle's workspace is reused). regen_attn_forward(h, q, k, v,
+ * o, s) equals this call with both ranges covering the window and lse NULL.
+ * Errors: INVALID_ARGUMENT (bad handle, range, pointer, alignment or
+ * overlap), HIP (launch failure).
+ */
+regen_status regen_attn_forward_range(regen_attn_t h, const void *q, int64_t q_begin,
+                                      int64_t q_count, const void *k, const void *v,
+                                      int64_t kv_begin, int64_t kv_count, void *o, float *lse,
+                                      void *stream);
+
+/*
+ * Combine nparts attention results over disjoint key sets into the result
+ * over their union (the exact combination Ring-style key splitting relies
+ * on; blog summary, "Methodology - deep read", USP paragraph):
+ *     lse = log sum_i exp(lse_i),   o = sum_i exp(lse_i - lse) o_i.
+ *   o_parts   : host array of nparts device pointers, each bf16
+ *               [heads][rows][head_dim], 16-byte aligned
+ *   lse_parts : host array of nparts device pointers, each fp32
+ *               [heads][rows], 4-byte aligned (-inf marks a part with no keys)
+ *   o         : bf16 [heads][rows][head_dim] output, 16-byte aligned
+ *   lse       : fp32 [heads][rows] output, or NULL
+ * 1 <= nparts <= 8; head_dim 64 or 128. Outputs must not overlap inputs. A
+ * row whose parts are all -inf gets o = 0 and lse = -inf. Needs no handle;
+ * enqueued on `stream` (the current device's). Errors: INVALID_ARGUMENT,
+ * UNSUPPORTED (head_dim), NO_DEVICE, HIP.
+ */
+regen_status regen_attn_merge(const void *const *o_parts, const float *const *lse_parts,
+                              int nparts, int heads, int64_t rows, int head_dim, void *o,
+                              float *lse, void *stream);
+
+/*
+ * The on-device halves of a Ulysses all-to-all (blog summary, "Methodology -
+ * deep read", USP paragraph: Ulysses reshuffles the sequence into attention
+ * heads; with G devices each holds tokens_local = N/G tokens of every head
+ * before attention and all N tokens of heads/G heads during it).
+ *
+ * regen_ulysses_pack: x [tokens_local][heads][head_dim] (this device's
+ * token shard, all heads) -> send [groups][tokens_local][heads/groups]
+ * [head_dim], so that block g (heads g*heads/groups ..) is one contiguous
+ * piece for device g. After the all-to-all, the piece received from device
+ * s is tokens s*tokens_local .. of this device's head group, i.e. the receive
+ * buffer is [N][heads/groups][head_dim] token-major: attention takes it as
+ * is with REGEN_ATTN_TOKEN_MAJOR (rotation fused into its loads) and writes
+ * O in the same layout, which is the send buffer of the reverse all-to-all.
+ *
+ * regen_ulysses_unpack: recv [groups][tokens_local][heads/groups][head_dim]
+ * (piece g from the device holding head group g) -> y [tokens_local][heads]
+ * [head_dim], this device's token shard with all heads again.
+ *
+ * bf16 elements; heads must be a multiple of groups and (heads/groups) *
+ * head_dim * 2 a multiple of 16; buffers 16-byte aligned, not overlapping.
+ * Enqueued on `stream` of the current device. Errors: INVALID_ARGUMENT,
+ * NO_DEVICE, HIP.
+ */
+regen_status regen_ulysses_pack(const void *x, void *send, int64_t tokens_local, int heads,
+                                int head_dim, int groups, void *stream);
+regen_status regen_ulysses_unpack(const void *recv, void *y, int64_t tokens_local, int heads,
+                                  int head_dim, int groups, void *stream);
 
 /*
  * Free the handle, its tables and workspace. No call on the handle may still

@@ -113,3 +113,38 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(native._build, "LIB", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         native.lib()
+
+
+def test_forward_range_rejects_non_live_handle():
+    fake = ctypes.c_void_p(0x1000)
+    s = native.regen_attn_forward_range(fake.value, 16, 0, 1, 16, 16, 0, 1, 32, None, None)
+    assert s == native.REGEN_ERR_INVALID_ARGUMENT
+    assert native.regen_attn_forward_range(None, 16, 0, 1, 16, 16, 0, 1, 32, None, None) == \
+        native.REGEN_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(nparts=0), native.REGEN_ERR_INVALID_ARGUMENT),
+    (dict(nparts=9), native.REGEN_ERR_INVALID_ARGUMENT),
+    (dict(heads=0), native.REGEN_ERR_INVALID_ARGUMENT),
+    (dict(rows=0), native.REGEN_ERR_INVALID_ARGUMENT),
+    (dict(head_dim=96), native.REGEN_ERR_UNSUPPORTED),
+    (dict(o=0), native.REGEN_ERR_INVALID_ARGUMENT),
+    (dict(o=0x10008), native.REGEN_ERR_INVALID_ARGUMENT),            # misaligned
+    (dict(null_part=True), native.REGEN_ERR_INVALID_ARGUMENT),
+    (dict(o=0x100000 + 64), native.REGEN_ERR_INVALID_ARGUMENT),      # overlaps part 0
+    (dict(), native.REGEN_ERR_NO_DEVICE),                            # valid, but no GPU here
+])
+def test_merge_argument_checks_before_the_device(kw, expect):
+    # Addresses are never dereferenced: every one of these fails before a
+    # kernel could be launched.
+    if expect == native.REGEN_ERR_NO_DEVICE and torch.cuda.is_available():
+        pytest.skip("host has a GPU: valid arguments would launch on these fake addresses")
+    n = kw.get("nparts", 2)
+    parts = [0x100000 + i * 0x100000 for i in range(max(n, 0))]
+    lses = [0x4000000 + i * 0x100000 for i in range(max(n, 0))]
+    if kw.get("null_part"):
+        parts[1] = 0
+    s = native.regen_attn_merge(parts, lses, kw.get("heads", 2), kw.get("rows", 8),
+                                kw.get("head_dim", 128), kw.get("o", 0x8000000), None, None)
+    assert s == expect, native.regen_attn_last_error()

@@ -432,3 +432,63 @@ def test_range_attention_matches_full_grid():
     qr = oracle.np_rope(q, w.grid)[:, qa:qb]
     kr = oracle.np_rope(k, w.grid)[:, ka:kb]
     np.testing.assert_allclose(o_r, oracle.np_attention(qr, kr, v[:, ka:kb]), rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Ulysses layouts (the on-device halves of the all-to-all)
+# --------------------------------------------------------------------------
+
+def test_ulysses_pack_unpack_elementwise_brute_force():
+    # Every element checked by index arithmetic written out in Python loops.
+    nl, h, d, groups = 5, 6, 4, 3
+    hg = h // groups
+    x = np.arange(nl * h * d).reshape(nl, h, d)
+    send = oracle.ulysses_pack(x, groups)
+    for g in range(groups):
+        for i in range(nl):
+            for j in range(hg):
+                for c in range(d):
+                    assert send[g, i, j, c] == x[i, g * hg + j, c]
+    y = oracle.ulysses_unpack(send)
+    for i in range(nl):
+        for hh in range(h):
+            for c in range(d):
+                assert y[i, hh, c] == send[hh // hg, i, hh % hg, c]
+    assert np.array_equal(y, x)  # unpack undoes pack
+
+
+@pytest.mark.parametrize("groups", [1, 2, 3, 4, 12])
+def test_ulysses_exchange_turns_token_shards_into_head_shards(groups):
+    # The defining property: after pack + all-to-all, device g holds all N
+    # tokens (in order) of head group g, i.e. X[:, g*Hg:(g+1)*Hg].
+    n, h, d = 24, 12, 8
+    x = RNG.standard_normal((n, h, d))
+    nl, hg = n // groups, h // groups
+    sends = [oracle.ulysses_pack(x[s * nl:(s + 1) * nl], groups) for s in range(groups)]
+    recvs = oracle.ulysses_exchange(sends)
+    for g in range(groups):
+        assert np.array_equal(recvs[g].reshape(n, hg, d), x[:, g * hg:(g + 1) * hg])
+    # and the reverse path (O in the same layout) restores the token shards
+    back = oracle.ulysses_exchange([r.reshape(n, hg, d).reshape(groups, nl, hg, d) for r in recvs])
+    for s in range(groups):
+        assert np.array_equal(oracle.ulysses_unpack(back[s]), x[s * nl:(s + 1) * nl])
+
+
+def test_ulysses_attention_equals_full_attention():
+    # Attention per head group on the exchanged (token-major) layout, sent
+    # back and unpacked, equals attention of the whole tensor.
+    w = synth.WORKLOADS["tiny_1x64_n128"]
+    groups, heads = 2, 4
+    qkv = [RNG.standard_normal((w.tokens, heads, w.head_dim)) for _ in range(3)]
+    nl, hg = w.tokens // groups, heads // groups
+    full = oracle.rope_attention(*(t.transpose(1, 0, 2) for t in qkv), w.grid)  # [H, N, d]
+    recvs = [oracle.ulysses_exchange([oracle.ulysses_pack(t[s * nl:(s + 1) * nl], groups)
+                                      for s in range(groups)]) for t in qkv]
+    outs = []
+    for g in range(groups):
+        q, k, v = (r[g].reshape(w.tokens, hg, w.head_dim).transpose(1, 0, 2) for r in recvs)
+        outs.append(oracle.rope_attention(q, k, v, w.grid).transpose(1, 0, 2)
+                    .reshape(groups, nl, hg, w.head_dim))
+    back = oracle.ulysses_exchange(outs)
+    got = np.concatenate([oracle.ulysses_unpack(back[s]) for s in range(groups)])  # [N, H, d]
+    np.testing.assert_allclose(got, full.transpose(1, 0, 2), rtol=0, atol=1e-13)
