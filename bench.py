@@ -39,6 +39,10 @@ def parse():
                     help="skip the Ulysses layout leg (profiling runs of the window alone)")
     ap.add_argument("--ulysses-only", action="store_true",
                     help="run only the Ulysses layout leg and print it")
+    ap.add_argument("--no-cross", action="store_true",
+                    help="skip the cross-attention leg (profiling runs of the window alone)")
+    ap.add_argument("--cross-only", action="store_true",
+                    help="run only the cross-attention leg and print it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run 3 device-to-device copies of this many MiB (to scale HBM "
                          "byte counters against a copy of known size) and exit")
@@ -172,6 +176,41 @@ def ring_split(w, qkv, stream, reps=10):
     }
 
 
+def cross_leg(w, reps=20):
+    """Cross-attention of the window's tokens to conditioning tokens (77,
+    the assumed encoder context, and 512): time per call against the HBM
+    roofline (reading Q and writing O dominate; the context is small)."""
+    import torch
+
+    from diffusion_transformer_attention_dit_amd import native, synth
+    stream = torch.cuda.current_stream()
+    q, _, _ = synth.make_qkv(w, device="cuda")
+    o = torch.empty_like(q)
+    attn = native.Attention(w.heads, w.head_dim, w.grid)
+    out = {"what": "all %d tokens x %d heads attend to ctx_len conditioning tokens, no rotation"
+                   % (w.tokens, w.heads)}
+    for ctx in (synth.CONTEXT_TOKENS, 512):
+        kc, vc = synth.make_context(w, ctx, device="cuda")
+        attn.forward_cross(q, kc, vc, out=o, stream=stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            attn.forward_cross(q, kc, vc, out=o, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / reps * 1e-3
+        flops = 4.0 * w.tokens * ctx * w.head_dim * w.heads
+        moved = 2 * w.heads * w.tokens * w.head_dim * 2 + 2 * w.heads * ctx * w.head_dim * 2
+        gbs = moved / t / 1e9
+        out["ctx_%d" % ctx] = {"us_per_call": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 2),
+                               "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                               "algorithmic_bytes": moved}
+    attn.close()
+    return out
+
+
 def ulysses_leg(w, groups=4, reps=20):
     """One device's share of Ulysses degree 4 at the window's shape: pack its
     token shard of Q for the all-to-all, attention of its head group on the
@@ -258,6 +297,9 @@ def main():
     native.lib()  # fail loudly if the HIP library is missing
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.cross_only:
+        print(json.dumps({"workload": w.name, "cross": cross_leg(w)}), flush=True)
+        return 0
     if args.ulysses_only:
         print(json.dumps({"workload": w.name, "ulysses": ulysses_leg(w)}), flush=True)
         return 0
@@ -355,6 +397,8 @@ def main():
         line["ring_split"] = ring_split(w, drv.inputs[0], stream)
     if not args.no_ulysses:
         line["ulysses"] = ulysses_leg(w)
+    if not args.no_cross:
+        line["cross"] = cross_leg(w)
     drv.close()
     del drv
     torch.cuda.empty_cache()

@@ -237,27 +237,30 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_
 // tiles, pass i giving tile i * P + p to workgroup p, so the workgroups that
 // share an XCD sweep the same head's keys together. The `rem` leftover
 // tiles (tiles >= full * P) are then cut stream-K style: their units are
-// split into P equal contiguous ranges, one per workgroup, so every slot
-// ends with the same amount of work. A leftover tile whose units span
-// several workgroups is finished by the merge kernel from the per-workgroup
-// partial results (unnormalised O, running max m, row sum l), combined
-// exactly as in blockwise softmax.
+// split into Prem = min(P, leftover units) equal contiguous ranges, one per
+// workgroup p < Prem, so every slot ends with the same amount of work and no
+// range is empty. A leftover tile whose units span several workgroups is
+// finished by the merge kernel from the per-workgroup partial results
+// (unnormalised O, running max m, row sum l), combined exactly as in
+// blockwise softmax.
 // ---------------------------------------------------------------------------
 struct Sched {
     int n_qtiles;         // query tiles per head
     int nkv;              // key blocks per tile
     int P;                // persistent workgroups
     int full;             // whole-tile passes
+    int Prem;             // workgroups sharing the leftover units, >= 1
     long long rem_units;  // units of the leftover tiles (rem * nkv)
 };
 
-// Start (offset into the leftover units) of workgroup p's leftover range.
+// Start (offset into the leftover units) of workgroup p's leftover range,
+// p <= Prem; ranges are non-empty because rem_units >= Prem.
 __device__ __forceinline__ long long rem_begin(const Sched& sc, int p) {
-    return (long long)p * sc.rem_units / sc.P;
+    return (long long)p * sc.rem_units / sc.Prem;
 }
 // The workgroup whose leftover range holds leftover unit y.
 __device__ __forceinline__ int rem_owner(const Sched& sc, long long y) {
-    return (int)(((y + 1) * sc.P - 1) / sc.rem_units);
+    return (int)(((y + 1) * sc.Prem - 1) / sc.rem_units);
 }
 // Partial-result slot of workgroup p for leftover tile t: the first tile of
 // its range uses 2p, a later (necessarily its last) tile uses 2p + 1.
@@ -276,6 +279,7 @@ __device__ __forceinline__ bool get_segment(const Sched& sc, int p, int k, long 
         *kv1 = sc.nkv;
         return true;
     }
+    if (p >= sc.Prem) return false;
     const long long base = (long long)sc.full * sc.P * sc.nkv;
     const long long a = base + rem_begin(sc, p), b = base + rem_begin(sc, p + 1);
     const long long x = (k == sc.full) ? a : (a / sc.nkv + (k - sc.full)) * sc.nkv;
@@ -572,12 +576,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 3: merge of split leftover tiles. Grid (rem tiles, BM): one block
-// per query row, 256 threads = 8 segment lanes x 32 groups of D/32 head
-// dims. A tile held whole by one workgroup returns at once. For row r:
-//   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s;
-// each segment lane folds every 8th segment, then the 8 lanes combine
-// through LDS the same way.
+// Kernel 3: merge of split leftover tiles. Grid (rem tiles, BM / 4): one
+// wave per query row, D/64 head dims per lane. A tile held whole by one
+// workgroup returns at once. For row r over the segments s holding it:
+//   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+//   lse = ln 2 (M + log2 sum_s 2^(m_s - M) l_s).
 // ---------------------------------------------------------------------------
 template <int D, int NW>
 __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -585,67 +588,52 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
                                                     const float* __restrict__ part_ml, int N,
                                                     Sched sc, long long qh, long long qn_stride) {
     constexpr int BM = NW * 32;
-    constexpr int DPT = D / 32;  // head dims per thread (4 or 2)
+    constexpr int DPL = D / 64;  // head dims per lane (2 or 1)
     const long long t = (long long)sc.full * sc.P + blockIdx.x;
     const long long y0 = (long long)blockIdx.x * sc.nkv;  // leftover unit offsets of tile t
     const int p0 = rem_owner(sc, y0);
     const int p1 = rem_owner(sc, y0 + sc.nkv - 1);
     if (p0 == p1) return;  // uniform over the block
     const int hd = (int)(t / sc.n_qtiles), qt = (int)(t % sc.n_qtiles);
-    const int r = blockIdx.y;
+    const int r = blockIdx.y * 4 + (int)(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int qrow = qt * BM + r;
-    if (qrow >= N) return;  // uniform over the block
-    const int sl = threadIdx.x / 32, d0 = (threadIdx.x % 32) * DPT;
+    if (qrow >= N) return;  // uniform over the wave
 
-    float Mi = -INFINITY;
-    for (int p = p0 + sl; p <= p1; p += 8)
-        Mi = fmaxf(Mi, part_ml[((size_t)partial_slot(sc, p, t) * BM + r) * 2]);
-    float Li = 0.0f, acc[DPT];
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) acc[i] = 0.0f;
-    for (int p = p0 + sl; p <= p1; p += 8) {
-        const int slot = partial_slot(sc, p, t);
-        const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((size_t)slot * BM + r) * 2);
-        const float w = __builtin_amdgcn_exp2f(ml.x - Mi);
-        Li += w * ml.y;
-        const float* po = part_o + ((size_t)slot * BM + r) * D + d0;
-#pragma unroll
-        for (int i = 0; i < DPT; ++i) acc[i] += w * po[i];
-    }
-
-    __shared__ float sm[8][32][DPT + 2];
-    sm[sl][threadIdx.x % 32][0] = Mi;
-    sm[sl][threadIdx.x % 32][1] = Li;
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) sm[sl][threadIdx.x % 32][2 + i] = acc[i];
-    __syncthreads();
-    if (sl != 0) return;
-    const int g = threadIdx.x;
+    // Partial slots: every workgroup after p0 starts its range inside tile
+    // t, so t is its first leftover tile (slot 2p); p0's range starts in t
+    // only if its first unit is t's first unit.
+    const int slot0 = partial_slot(sc, p0, t);
+    auto slot_of = [&](int p) { return p == p0 ? slot0 : 2 * p; };
     float M = -INFINITY;
+#pragma unroll 8
+    for (int p = p0; p <= p1; ++p) M = fmaxf(M, part_ml[((size_t)slot_of(p) * BM + r) * 2]);
+    float L = 0.0f, acc[DPL];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) M = fmaxf(M, sm[k][g][0]);
-    float L = 0.0f, out[DPT];
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) out[i] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const float Mk = sm[k][g][0];
-        if (Mk == -INFINITY) continue;  // lane without segments
-        const float w = __builtin_amdgcn_exp2f(Mk - M);
-        L += w * sm[k][g][1];
-#pragma unroll
-        for (int i = 0; i < DPT; ++i) out[i] += w * sm[k][g][2 + i];
+    for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
+#pragma unroll 8
+    for (int p = p0; p <= p1; ++p) {
+        const int slot = slot_of(p);
+        const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((size_t)slot * BM + r) * 2);
+        const float w = __builtin_amdgcn_exp2f(ml.x - M);
+        L += w * ml.y;
+        const float* po = part_o + ((size_t)slot * BM + r) * D + lane * DPL;
+        if constexpr (DPL == 2) {
+            const float2 x = *reinterpret_cast<const float2*>(po);
+            acc[0] += w * x.x;
+            acc[1] += w * x.y;
+        } else {
+            acc[0] += w * po[0];
+        }
     }
     const float inv = 1.0f / L;
-    if (lse != nullptr && g == 0) lse[(size_t)hd * N + qrow] = (M + log2f(L)) * 0.69314718055994531f;
-    uint16_t* op = o + hd * qh + qrow * qn_stride + d0;
-    if constexpr (DPT == 4) {
-        uint2 w2;
-        w2.x = pack_bf16(out[0] * inv, out[1] * inv);
-        w2.y = pack_bf16(out[2] * inv, out[3] * inv);
-        *reinterpret_cast<uint2*>(op) = w2;
+    if (lse != nullptr && lane == 0) lse[(size_t)hd * N + qrow] = (M + log2f(L)) * 0.69314718055994531f;
+    uint16_t* op = o + hd * qh + qrow * qn_stride + lane * DPL;
+    if constexpr (DPL == 2) {
+        *reinterpret_cast<uint32_t*>(op) = pack_bf16(acc[0] * inv, acc[1] * inv);
     } else {
-        *reinterpret_cast<uint32_t*>(op) = pack_bf16(out[0] * inv, out[1] * inv);
+        const uint32_t w2 = pack_bf16(acc[0] * inv, 0.0f);
+        *op = (uint16_t)(w2 & 0xffffu);
     }
 }
 

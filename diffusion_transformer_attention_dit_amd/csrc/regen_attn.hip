@@ -125,7 +125,8 @@ struct regen_attn {
     std::vector<ProfRecord> prof_free;     // created, reusable
     Problem p;
     regen::RopeGeom geo;
-    float2* d_tab;   // rotary (cos, sin) per axis
+    float2* d_tab;     // rotary (cos, sin) per axis
+    float2* d_tab_id;  // the same table with every angle 0 (unrotated calls)
     uint16_t* d_kr;  // workspace: rotated K
     uint16_t* d_vt;  // workspace: transposed V
     int P;           // persistent attention workgroups
@@ -223,7 +224,7 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
     h->device = dev;
     h->p = p;
     h->geo = geo;
-    h->d_tab = nullptr;
+    h->d_tab = h->d_tab_id = nullptr;
     h->d_kr = h->d_vt = nullptr;
     h->d_part_o = h->d_part_ml = nullptr;
     int per_cu = 1;
@@ -247,7 +248,7 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
     };
     const size_t part_o_bytes = size_t(2) * h->P * kBM * p.head_dim * sizeof(float);
     const size_t part_ml_bytes = size_t(2) * h->P * kBM * 2 * sizeof(float);
-    if ((e = hipMalloc(&h->d_tab, tab_bytes)) != hipSuccess ||
+    if ((e = hipMalloc(&h->d_tab, 2 * tab_bytes)) != hipSuccess ||
         (e = hipMalloc(&h->d_kr, half_ws)) != hipSuccess ||
         (e = hipMalloc(&h->d_vt, half_ws)) != hipSuccess ||
         (e = hipMalloc(&h->d_part_o, part_o_bytes)) != hipSuccess ||
@@ -257,7 +258,9 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
         return fail(e == hipErrorOutOfMemory ? REGEN_ERR_OUT_OF_MEMORY : REGEN_ERR_HIP,
                     std::string("device allocation failed: ") + hipGetErrorString(e));
     }
-    if ((e = hipMemcpy(h->d_tab, tab.data(), tab_bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+    h->d_tab_id = h->d_tab + tab.size();
+    tab.resize(2 * tab.size(), float2{1.0f, 0.0f});
+    if ((e = hipMemcpy(h->d_tab, tab.data(), 2 * tab_bytes, hipMemcpyHostToDevice)) != hipSuccess) {
         cleanup();
         return fail_hip(e, "hipMemcpy of the rotary table");
     }
@@ -282,14 +285,18 @@ bool overlaps(uintptr_t a, uintptr_t na, uintptr_t b, uintptr_t nb) {
 // tokens [kv_begin, kv_begin + nk) of the handle's window.
 regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, const void* k,
                     const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse,
-                    void* stream) {
+                    void* stream, bool cross = false) {
     if (!h || !is_live(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is NULL or not live");
     if (!q || !k || !v || !o) return fail(REGEN_ERR_INVALID_ARGUMENT, "q, k, v, o must be non-NULL");
     const Problem& p = h->p;
     if (q_begin < 0 || nq < 1 || q_begin + nq > p.tokens)
         return fail(REGEN_ERR_INVALID_ARGUMENT, "query range outside [0, grid_t*grid_h*grid_w)");
-    if (kv_begin < 0 || nk < 1 || kv_begin + nk > p.tokens)
+    if (cross) {
+        if (nk < 1 || nk > p.tokens)
+            return fail(REGEN_ERR_INVALID_ARGUMENT, "ctx_len must be in [1, grid_t*grid_h*grid_w]");
+    } else if (kv_begin < 0 || nk < 1 || kv_begin + nk > p.tokens) {
         return fail(REGEN_ERR_INVALID_ARGUMENT, "key range outside [0, grid_t*grid_h*grid_w)");
+    }
     const uintptr_t ptrs[4] = {uintptr_t(q), uintptr_t(k), uintptr_t(v), uintptr_t(o)};
     for (uintptr_t a : ptrs)
         if (a % 16 != 0) return fail(REGEN_ERR_INVALID_ARGUMENT, "q, k, v, o must be 16-byte aligned");
@@ -327,12 +334,15 @@ regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, 
     sc.full = int(tiles / h->P);
     const int64_t rem_tiles = tiles - int64_t(sc.full) * h->P;
     sc.rem_units = rem_tiles * sc.nkv;
-    const dim3 mgrid{unsigned(rem_tiles), unsigned(kBM), 1u};
+    sc.Prem = int(sc.rem_units < h->P ? (sc.rem_units > 0 ? sc.rem_units : 1) : h->P);
+    const dim3 mgrid{unsigned(rem_tiles), unsigned(kBM / 4), 1u};
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
     const uint16_t* k16 = static_cast<const uint16_t*>(k);
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
     uint16_t* o16 = static_cast<uint16_t*>(o);
     const int q_off = int(q_begin), k_off = int(kv_begin);
+    // Cross-attention rotates nothing: the identity table.
+    const float2* tab = cross ? h->d_tab_id : h->d_tab;
     // Element strides of (head, token) in q/o and in k/v.
     const bool tm = (p.flags & REGEN_ATTN_TOKEN_MAJOR) != 0;
     const long long D = p.head_dim;
@@ -362,10 +372,10 @@ regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, 
 
     if (p.head_dim == 128) {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<128>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
-                           h->d_vt, h->d_tab, h->geo, Nk, Npad, k_off, kh, kn);
+                           h->d_vt, tab, h->geo, Nk, Npad, k_off, kh, kn);
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<128, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
-                           st, q16, h->d_kr, h->d_vt, o16, lse, h->d_tab, h->geo, Nq, Nk, Npad,
+                           st, q16, h->d_kr, h->d_vt, o16, lse, tab, h->geo, Nq, Nk, Npad,
                            q_off, qh, qn, sc, c2, h->d_part_o, h->d_part_ml);
         mark(2);
         if (rem_tiles > 0)
@@ -373,10 +383,10 @@ regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, 
                                h->d_part_o, h->d_part_ml, Nq, sc, qh, qn);
     } else {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
-                           h->d_vt, h->d_tab, h->geo, Nk, Npad, k_off, kh, kn);
+                           h->d_vt, tab, h->geo, Nk, Npad, k_off, kh, kn);
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<64, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
-                           st, q16, h->d_kr, h->d_vt, o16, lse, h->d_tab, h->geo, Nq, Nk, Npad,
+                           st, q16, h->d_kr, h->d_vt, o16, lse, tab, h->geo, Nq, Nk, Npad,
                            q_off, qh, qn, sc, c2, h->d_part_o, h->d_part_ml);
         mark(2);
         if (rem_tiles > 0)
@@ -409,6 +419,14 @@ regen_status regen_attn_forward_range(regen_attn_t h, const void* q, int64_t q_b
                                       void* stream) {
     g_last_error.clear();
     return launch(h, q, q_begin, q_count, k, v, kv_begin, kv_count, o, lse, stream);
+}
+
+regen_status regen_attn_forward_cross(regen_attn_t h, const void* q, const void* k_ctx,
+                                      const void* v_ctx, int64_t ctx_len, void* o, float* lse,
+                                      void* stream) {
+    g_last_error.clear();
+    if (!h || !is_live(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is NULL or not live");
+    return launch(h, q, 0, h->p.tokens, k_ctx, v_ctx, 0, ctx_len, o, lse, stream, true);
 }
 
 regen_status regen_attn_merge(const void* const* o_parts, const float* const* lse_parts,

@@ -25,6 +25,7 @@ EXPORTS = (
     "regen_attn_create",
     "regen_attn_forward",
     "regen_attn_forward_range",
+    "regen_attn_forward_cross",
     "regen_attn_merge",
     "regen_ulysses_pack",
     "regen_ulysses_unpack",
@@ -84,6 +85,8 @@ def lib():
     i64 = ctypes.c_int64
     L.regen_attn_forward_range.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, vp, vp, vp]
     L.regen_attn_forward_range.restype = ctypes.c_int
+    L.regen_attn_forward_cross.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp]
+    L.regen_attn_forward_cross.restype = ctypes.c_int
     L.regen_attn_merge.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int,
                                    ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
     L.regen_attn_merge.restype = ctypes.c_int
@@ -134,6 +137,10 @@ def regen_attn_forward_range(handle, q, q_begin, q_count, k, v, kv_begin, kv_cou
     """Pointers are integer device addresses (lse may be 0 / None)."""
     return lib().regen_attn_forward_range(handle, q, q_begin, q_count, k, v, kv_begin, kv_count,
                                           o, lse or None, stream)
+
+
+def regen_attn_forward_cross(handle, q, k_ctx, v_ctx, ctx_len, o, lse, stream):
+    return lib().regen_attn_forward_cross(handle, q, k_ctx, v_ctx, ctx_len, o, lse or None, stream)
 
 
 def regen_attn_merge(o_parts, lse_parts, heads, rows, head_dim, o, lse, stream):
@@ -310,6 +317,30 @@ class Attention:
                                      stream.cuda_stream)
         if s != REGEN_OK:
             raise RegenAttnError(s, "regen_attn_forward_range")
+        return out, (lse if lse is not False else None)
+
+    def forward_cross(self, q, k_ctx, v_ctx, out=None, lse=False, stream=None):
+        """All window tokens q against context keys/values (no rotation).
+        Returns (o, lse or None); pass lse=None to have it allocated."""
+        import torch
+        tm = bool(self.desc.flags & REGEN_ATTN_TOKEN_MAJOR)
+        nc = int(k_ctx.shape[0] if tm else k_ctx.shape[1])
+        self._check(q, "q")
+        self._check_rows(k_ctx, nc, "k_ctx")
+        self._check_rows(v_ctx, nc, "v_ctx")
+        if out is None:
+            out = torch.empty_like(q)
+        self._check(out, "out")
+        if lse is None:
+            lse = torch.empty((self.heads, self.tokens), dtype=torch.float32, device=q.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        s = regen_attn_forward_cross(self.handle, q.data_ptr(), k_ctx.data_ptr(), v_ctx.data_ptr(),
+                                     nc, out.data_ptr(),
+                                     lse.data_ptr() if lse is not False else None,
+                                     stream.cuda_stream)
+        if s != REGEN_OK:
+            raise RegenAttnError(s, "regen_attn_forward_cross")
         return out, (lse if lse is not False else None)
 
     def _check_rows(self, t, n, name):

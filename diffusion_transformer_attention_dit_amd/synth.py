@@ -95,6 +95,25 @@ def make_qkv(w: Workload, step: int = 0, block: int = 0, device="cpu", base_seed
     return q, k, v
 
 
+# Conditioning context length for cross-attention. The pages name the
+# text/image encoders the decoder is conditioned on but not how many tokens
+# they hand over; 77 is the CLIP text encoder's fixed context.
+CONTEXT_TOKENS = 77
+
+
+def make_context(w: Workload, ctx_len: int = CONTEXT_TOKENS, step: int = 0, block: int = 0,
+                 device="cpu", base_seed: int = 0, dtype: torch.dtype = torch.bfloat16):
+    """Draw conditioning keys and values (k_ctx, v_ctx), each
+    [heads, ctx_len, head_dim], N(0,1) * the workload's std, from a seed of
+    their own (independent of make_qkv's)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(w, step, block, base_seed) ^ 0x5EED_C7C7)
+    shape = (w.heads, ctx_len, w.head_dim)
+    k = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * w.std
+    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * w.std
+    return k.to(dtype).contiguous(), v.to(dtype).contiguous()
+
+
 def sample_rows(n: int, count: int, seed: int, tile: int = 128):
     """A seeded sorted sample of query rows that always holds the first and
     last row and the rows on each side of every `tile` boundary it can fit."""

@@ -158,6 +158,24 @@ regen_status regen_attn_forward_range(regen_attn_t h, const void *q, int64_t q_b
                                       void *stream);
 
 /*
+ * Cross-attention of the window's tokens to conditioning tokens (the text /
+ * image encoder context a DiT block attends to besides its own tokens; the
+ * pages name the encoders, not the context length): for every head and
+ * window token m, o_m = sum_j softmax_j(sm_scale <q_m, c_j>) w_j over the
+ * ctx_len context keys c_j and values w_j. Nothing is rotated.
+ *   q      : all window tokens, layout as for regen_attn_forward
+ *   k_ctx, v_ctx : [heads][ctx_len][head_dim] bf16 ([ctx_len][heads]
+ *            [head_dim] with REGEN_ATTN_TOKEN_MAJOR)
+ *   o      : like q;  lse : [heads][tokens] fp32 or NULL
+ * 1 <= ctx_len <= grid_t*grid_h*grid_w (the workspace is sized by the
+ * window). Same pointer rules, ordering rule and errors as
+ * regen_attn_forward_range.
+ */
+regen_status regen_attn_forward_cross(regen_attn_t h, const void *q, const void *k_ctx,
+                                      const void *v_ctx, int64_t ctx_len, void *o, float *lse,
+                                      void *stream);
+
+/*
  * Combine nparts attention results over disjoint key sets into the result
  * over their union (the exact combination Ring-style key splitting relies
  * on; blog summary, "Methodology - deep read", USP paragraph):

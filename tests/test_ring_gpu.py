@@ -218,3 +218,25 @@ def test_range_argument_errors_on_device():
     assert s == L.REGEN_ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
     attn.close()
+
+
+def test_short_key_run_after_large_logit_call():
+    # Regression: with fewer leftover (tile, key block) units than resident
+    # workgroups, no workgroup may sit idle inside a split tile's owner
+    # range, or the split-tile merge would read partial results a previous
+    # call left behind. The first call leaves large running maxima in the
+    # scratch; the short key run that follows must not see them.
+    w = synth.WORKLOADS["window25_12x128_n10920"]
+    say("case short key run after a large-logit call (same handle)")
+    q, k, v = synth.make_qkv(w, 2, 2, device="cuda")
+    attn = native.Attention(w.heads, w.head_dim, w.grid)
+    attn.forward((q.float() * 6).to(torch.bfloat16), (k.float() * 6).to(torch.bfloat16), v)
+    nk = 100
+    o, lse = attn.forward_range(q, 0, k[:, :nk].contiguous(), v[:, :nk].contiguous(), 0)
+    torch.cuda.synchronize()
+    attn.close()
+    rows = synth.sample_rows(w.tokens, 128, seed=21)
+    ref_o, ref_lse = oracle.rope_attention_range(f64(q), f64(k[:, :nk]), f64(v[:, :nk]), w.grid,
+                                                 0, 0, rows=rows)
+    check_o(f64(o)[:, rows], ref_o, "short run")
+    check_lse(lse.cpu().double().numpy()[:, rows], ref_lse, "short run")
