@@ -43,6 +43,10 @@ def parse():
                     help="skip the cross-attention leg (profiling runs of the window alone)")
     ap.add_argument("--cross-only", action="store_true",
                     help="run only the cross-attention leg and print it")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the attention-block leg (profiling runs of the window alone)")
+    ap.add_argument("--block-only", action="store_true",
+                    help="run only the attention-block leg and print it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run 3 device-to-device copies of this many MiB (to scale HBM "
                          "byte counters against a copy of known size) and exit")
@@ -176,6 +180,58 @@ def ring_split(w, qkv, stream, reps=10):
     }
 
 
+def block_leg(w, reps=10):
+    """One self-attention block with random-init weights: QKV projection,
+    3D-RoPE attention, output projection, timed as one unit, at the 1560-token
+    block workload (12 x 128); the projection GEMM alone is also timed at the
+    window's size."""
+    import torch
+
+    from diffusion_transformer_attention_dit_amd import native, synth
+    window = w
+    w = synth.WORKLOADS["block_12x128_n1560"]
+    stream = torch.cuda.current_stream()
+    x, w_qkv, w_o = synth.make_block_inputs(w, device="cuda")
+    y = torch.empty_like(x)
+    blk = native.Block(w.heads, w.head_dim, w.grid)
+    blk.forward(x, w_qkv, w_o, out=y, stream=stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        blk.forward(x, w_qkv, w_o, out=y, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    blk.close()
+    t = a.elapsed_time(b) / reps * 1e-3
+    hid = w.heads * w.head_dim
+    gemm = 2.0 * w.tokens * hid * 3 * hid + 2.0 * w.tokens * hid * hid
+    total = gemm + w.flops_per_call
+    # The QKV projection GEMM alone at the window's token count.
+    g = torch.Generator(device="cuda").manual_seed(5)
+    xw = torch.randn(window.tokens, hid, generator=g, device="cuda").to(torch.bfloat16)
+    wq = (torch.randn(3 * hid, hid, generator=g, device="cuda") * hid ** -0.5).to(torch.bfloat16)
+    yq = torch.empty(window.tokens, 3 * hid, dtype=torch.bfloat16, device="cuda")
+    native.linear(xw, wq, out=yq, stream=stream)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        native.linear(xw, wq, out=yq, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    tg = a.elapsed_time(b) / reps * 1e-3
+    gf = 2.0 * window.tokens * hid * 3 * hid
+    return {"what": "x[%d, %d] -> [Q|K|V] = x W_qkv^T -> attention -> y = O W_o^T (bf16, "
+                    "random-init weights)" % (w.tokens, hid),
+            "workload": w.name, "ms_per_block": round(t * 1e3, 4), "gflop": round(total / 1e9, 1),
+            "tflops": round(total / t / 1e12, 2), "pct_peak": round(100 * total / t / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "projection_gflop": round(gemm / 1e9, 1), "attention_gflop": round(w.flops_per_call / 1e9, 1),
+            "qkv_projection_window": {"kernel": "gemm_nt_kernel", "shape": [window.tokens, hid, 3 * hid],
+                                      "avg_launch_us": round(tg * 1e6, 2), "bound": "mfma",
+                                      "achieved": round(gf / tg / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": round(gf / tg / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+
+
 def cross_leg(w, reps=20):
     """Cross-attention of the window's tokens to conditioning tokens (77,
     the assumed encoder context, and 512): time per call against the HBM
@@ -297,6 +353,9 @@ def main():
     native.lib()  # fail loudly if the HIP library is missing
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.block_only:
+        print(json.dumps({"workload": w.name, "block": block_leg(w)}), flush=True)
+        return 0
     if args.cross_only:
         print(json.dumps({"workload": w.name, "cross": cross_leg(w)}), flush=True)
         return 0
@@ -399,6 +458,8 @@ def main():
         line["ulysses"] = ulysses_leg(w)
     if not args.no_cross:
         line["cross"] = cross_leg(w)
+    if not args.no_block:
+        line["block"] = block_leg(w)
     drv.close()
     del drv
     torch.cuda.empty_cache()

@@ -293,8 +293,9 @@ __device__ __forceinline__ bool get_segment(const Sched& sc, int p, int k, long 
 
 // ---------------------------------------------------------------------------
 // Kernel 2: attention, persistent. Grid P, NW * 64 threads.
-//   q, o    : bf16, row m of head h at element h * qh + m * qn (head-major or
-//             token-major as for kernel 1), row m being token q_off + m
+//   q, o    : bf16, row m of head h at element h * qh + m * qn of q and
+//             h * oh + m * on of o (head-major, token-major or a strided
+//             token-major view), row m being token q_off + m
 //   Kr, Vt  : the Nk keys prepared by kernel 1 (Npad rows per head)
 //   lse     : [heads][Nq] fp32 log-sum-exp of each row's scores, or null
 //   part_o  : [2P][BM][D] fp32 unnormalised O of split tiles
@@ -305,8 +306,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, float* __restrict__ lse,
     const float2* __restrict__ tab, RopeGeom geo, int Nq, int Nk, int Npad, int q_off,
-    long long qh, long long qn_stride, Sched sc, float c2 /* sm_scale * log2(e) */,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    long long qh, long long qn_stride, long long oh, long long on_stride, Sched sc,
+    float c2 /* sm_scale * log2(e) */, float* __restrict__ part_o, float* __restrict__ part_ml) {
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(BN == 64 || BN == 128, "key tile");
     constexpr int BM = NW * 32;
@@ -538,7 +539,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             if (qrow < Nq) {
                 if (lse != nullptr && half == 0)
                     lse[(size_t)hd * Nq + qrow] = (m_run + log2f(l_row)) * 0.69314718055994531f;
-                uint16_t* op = o + hd * qh + qrow * qn_stride;
+                uint16_t* op = o + hd * oh + qrow * on_stride;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -586,7 +587,7 @@ template <int D, int NW>
 __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, float* __restrict__ lse,
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml, int N,
-                                                    Sched sc, long long qh, long long qn_stride) {
+                                                    Sched sc, long long oh, long long on_stride) {
     constexpr int BM = NW * 32;
     constexpr int DPL = D / 64;  // head dims per lane (2 or 1)
     const long long t = (long long)sc.full * sc.P + blockIdx.x;
@@ -628,7 +629,7 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
     }
     const float inv = 1.0f / L;
     if (lse != nullptr && lane == 0) lse[(size_t)hd * N + qrow] = (M + log2f(L)) * 0.69314718055994531f;
-    uint16_t* op = o + hd * qh + qrow * qn_stride + lane * DPL;
+    uint16_t* op = o + hd * oh + qrow * on_stride + lane * DPL;
     if constexpr (DPL == 2) {
         *reinterpret_cast<uint32_t*>(op) = pack_bf16(acc[0] * inv, acc[1] * inv);
     } else {
@@ -714,6 +715,97 @@ __global__ __launch_bounds__(256) void block_transpose_kernel(const uint4* __res
     const long long e = i % E16, ba = i / E16;
     const long long a = ba % A, b = ba / A;
     dst[i] = src[(a * B + b) * E16 + e];
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 6: a linear layer without bias, C = A B^T: A [M][K] (row stride
+// lda), B [N][K] (row stride ldb: the [out][in] weight of the layer), C [M][N]
+// (row stride ldc); bf16 in, fp32 accumulation, bf16 out (RNE). K % 64 == 0.
+// Tile 128 x 128 per workgroup of 4 waves (64 x 64 each, 2 x 2 MFMA
+// blocks), K steps of 64 through double-buffered LDS filled by LDS-DMA copies
+// (128-byte rows, chunk ^ ((row >> 1) & 7)). Rows past M or N read as zero
+// (buffer resources) and are not stored.
+// ---------------------------------------------------------------------------
+constexpr int kGemmTile = 128, kGemmBK = 64;
+
+// Copies of one 128-row x 64-k tile (16 KiB, 16 runs of 1 KiB, 4 per wave).
+__device__ __forceinline__ void gemm_issue(__amdgpu_buffer_rsrc_t rs, int ld, int row0, int k0,
+                                           char* lds, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int run = i * 4 + wave;
+        const int p = run * 64 + lane;  // chunk position in the tile
+        const int r = p >> 3, pc = p & 7;
+        const int c = pc ^ ((r >> 1) & 7);  // the logical chunk stored at pc
+        g2lds16(rs, (uint32_t)(((long long)(row0 + r) * ld + k0 + c * 8) * 2), lds + run * 1024);
+    }
+}
+
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict__ A, int lda,
+                                                      const uint16_t* __restrict__ B, int ldb,
+                                                      uint16_t* __restrict__ C, int ldc, int M,
+                                                      int N, int K) {
+    constexpr int TB = kGemmTile * kGemmBK * 2;  // bytes of one tile
+    __shared__ __attribute__((aligned(1024))) char smem[2][2][TB];  // [buffer][A, B]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.x * kGemmTile, n0 = blockIdx.y * kGemmTile;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)((long long)M * lda * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)((long long)N * ldb * 2));
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    gemm_issue(ra, lda, m0, 0, smem[0][0], wave, lane);
+    gemm_issue(rb, ldb, n0, 0, smem[0][1], wave, lane);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int nk = K / kGemmBK;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) {
+            gemm_issue(ra, lda, m0, (kt + 1) * kGemmBK, smem[buf ^ 1][0], wave, lane);
+            gemm_issue(rb, ldb, n0, (kt + 1) * kGemmBK, smem[buf ^ 1][1], wave, lane);
+        }
+        const char* as = smem[buf][0];
+        const char* bs = smem[buf][1];
+#pragma unroll
+        for (int kk = 0; kk < kGemmBK / 16; ++kk) {
+            bf16x8 a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(as + swz_off<128>(wm * 64 + i * 32 + col, kk * 2 + half));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(bs + swz_off<128>(wn * 64 + j * 32 + col, kk * 2 + half));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    // Lane (col, half) holds C[m][n] for n = its column and 16 rows m.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + wn * 64 + j * 32 + col;
+            if (n >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 64 + i * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+                if (m < M) C[(long long)m * ldc + n] = (uint16_t)(pack_bf16(acc[i][j][r], 0.0f) & 0xffffu);
+            }
+        }
 }
 
 }  // namespace regen

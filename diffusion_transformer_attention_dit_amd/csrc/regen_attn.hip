@@ -281,6 +281,15 @@ bool overlaps(uintptr_t a, uintptr_t na, uintptr_t b, uintptr_t nb) {
     return a < b + nb && b < a + na;
 }
 
+// Element strides of (head, token) in q, k/v and o.
+struct Strides {
+    long long qh, qn, kh, kn, oh, on;
+};
+
+regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, const void* k,
+                     const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse,
+                     void* stream, bool cross, const Strides& sd);
+
 // One attention call: query tokens [q_begin, q_begin + nq) against key
 // tokens [kv_begin, kv_begin + nk) of the handle's window.
 regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, const void* k,
@@ -314,6 +323,21 @@ regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, 
                 overlaps(uintptr_t(lse), lbytes, ptrs[3], qbytes)))
         return fail(REGEN_ERR_INVALID_ARGUMENT, "lse overlaps q, k, v or o");
 
+    const bool tm = (p.flags & REGEN_ATTN_TOKEN_MAJOR) != 0;
+    const long long D = p.head_dim;
+    Strides sd;
+    sd.qh = sd.oh = tm ? D : nq * D;
+    sd.qn = sd.on = tm ? p.heads * D : D;
+    sd.kh = tm ? D : nk * D;
+    sd.kn = tm ? p.heads * D : D;
+    return enqueue(h, q, q_begin, nq, k, v, kv_begin, nk, o, lse, stream, cross, sd);
+}
+
+// Enqueue the kernels of one call whose arguments have been checked.
+regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, const void* k,
+                     const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse,
+                     void* stream, bool cross, const Strides& sd) {
+    const Problem& p = h->p;
     int cur = -1;
     hipError_t ge = hipGetDevice(&cur);
     if (ge != hipSuccess) return fail_hip(ge, "hipGetDevice");
@@ -343,11 +367,7 @@ regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, 
     const int q_off = int(q_begin), k_off = int(kv_begin);
     // Cross-attention rotates nothing: the identity table.
     const float2* tab = cross ? h->d_tab_id : h->d_tab;
-    // Element strides of (head, token) in q/o and in k/v.
-    const bool tm = (p.flags & REGEN_ATTN_TOKEN_MAJOR) != 0;
-    const long long D = p.head_dim;
-    const long long qh = tm ? D : nq * D, qn = tm ? p.heads * D : D;
-    const long long kh = tm ? D : nk * D, kn = tm ? p.heads * D : D;
+    const long long qh = sd.qh, qn = sd.qn, kh = sd.kh, kn = sd.kn, oh = sd.oh, on = sd.on;
 
     ProfRecord rec{};
     const bool prof = (p.flags & REGEN_ATTN_PROFILE) != 0;
@@ -376,22 +396,22 @@ regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, 
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<128, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
                            st, q16, h->d_kr, h->d_vt, o16, lse, tab, h->geo, Nq, Nk, Npad,
-                           q_off, qh, qn, sc, c2, h->d_part_o, h->d_part_ml);
+                           q_off, qh, qn, oh, on, sc, c2, h->d_part_o, h->d_part_ml);
         mark(2);
         if (rem_tiles > 0)
             hipLaunchKernelGGL((regen::merge_kernel<128, kNW>), mgrid, dim3(256), 0, st, o16, lse,
-                               h->d_part_o, h->d_part_ml, Nq, sc, qh, qn);
+                               h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
     } else {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
                            h->d_vt, tab, h->geo, Nk, Npad, k_off, kh, kn);
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<64, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
                            st, q16, h->d_kr, h->d_vt, o16, lse, tab, h->geo, Nq, Nk, Npad,
-                           q_off, qh, qn, sc, c2, h->d_part_o, h->d_part_ml);
+                           q_off, qh, qn, oh, on, sc, c2, h->d_part_o, h->d_part_ml);
         mark(2);
         if (rem_tiles > 0)
             hipLaunchKernelGGL((regen::merge_kernel<64, kNW>), mgrid, dim3(256), 0, st, o16, lse,
-                               h->d_part_o, h->d_part_ml, Nq, sc, qh, qn);
+                               h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
     }
     hipError_t e = hipGetLastError();
     if (prof) {
@@ -596,6 +616,167 @@ regen_status regen_attn_destroy(regen_attn_t h) {
             for (hipEvent_t ev : r.ev) (void)hipEventDestroy(ev);
     if (switched) (void)hipSetDevice(cur);
     delete h;
+    return REGEN_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Linear layers and the self-attention block
+//   [Q | K | V] = X W_qkv^T,  O = attention(R Q, R K, V),  Y = O W_o^T.
+// The projections run in gemm_nt_kernel; attention reads Q, K, V straight out
+// of the fused projection output as strided token-major views and writes its
+// output token-major, so nothing is copied between the three steps.
+// ---------------------------------------------------------------------------
+struct regen_block {
+    regen_attn* attn;    // attention of the block (internal handle)
+    int N, hidden;
+    uint16_t* qkv;       // [N][3 hidden]
+    uint16_t* attn_out;  // [N][hidden]
+};
+
+namespace {
+
+std::mutex g_blocks_mu;
+std::unordered_set<const void*> g_blocks;
+
+bool block_live(const void* b) {
+    std::lock_guard<std::mutex> lk(g_blocks_mu);
+    return g_blocks.count(b) != 0;
+}
+
+void block_free(regen_block* b) {
+    if (!b) return;
+    if (b->qkv) (void)hipFree(b->qkv);
+    if (b->attn_out) (void)hipFree(b->attn_out);
+    if (b->attn) (void)regen_attn_destroy(b->attn);
+    delete b;
+}
+
+void gemm(const uint16_t* A, int lda, const uint16_t* B, int ldb, uint16_t* C, int ldc, int M, int N,
+          int K, hipStream_t st) {
+    const dim3 grid{unsigned((M + regen::kGemmTile - 1) / regen::kGemmTile),
+                    unsigned((N + regen::kGemmTile - 1) / regen::kGemmTile), 1u};
+    hipLaunchKernelGGL(regen::gemm_nt_kernel, grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K);
+}
+
+}  // namespace
+
+extern "C" {
+
+regen_status regen_linear(const void* x, const void* w, void* y, int64_t rows, int in_features,
+                          int out_features, void* stream) {
+    g_last_error.clear();
+    if (!x || !w || !y) return fail(REGEN_ERR_INVALID_ARGUMENT, "x, w, y must be non-NULL");
+    if (rows < 1 || in_features < 1 || out_features < 1)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "rows, in_features, out_features must be >= 1");
+    if (in_features % regen::kGemmBK != 0)
+        return fail(REGEN_ERR_UNSUPPORTED, "in_features must be a multiple of 64");
+    if (rows > (int64_t(1) << 30) || in_features > (1 << 20) || out_features > (1 << 20) ||
+        rows * in_features * 2 >= (int64_t(1) << 32) ||
+        int64_t(out_features) * in_features * 2 >= (int64_t(1) << 32))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "an operand exceeds 4 GiB");
+    const uintptr_t ptrs[3] = {uintptr_t(x), uintptr_t(w), uintptr_t(y)};
+    for (uintptr_t a : ptrs)
+        if (a % 16 != 0) return fail(REGEN_ERR_INVALID_ARGUMENT, "x, w, y must be 16-byte aligned");
+    const uintptr_t xb = uintptr_t(rows) * in_features * 2, wb = uintptr_t(out_features) * in_features * 2,
+                    yb = uintptr_t(rows) * out_features * 2;
+    if (overlaps(ptrs[2], yb, ptrs[0], xb) || overlaps(ptrs[2], yb, ptrs[1], wb))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "y overlaps x or w");
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count < 1) {
+        (void)hipGetLastError();
+        return fail(REGEN_ERR_NO_DEVICE, "no HIP device is available");
+    }
+    gemm(static_cast<const uint16_t*>(x), in_features, static_cast<const uint16_t*>(w), in_features,
+         static_cast<uint16_t*>(y), out_features, int(rows), out_features, in_features,
+         static_cast<hipStream_t>(stream));
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    return REGEN_OK;
+}
+
+regen_status regen_block_create(const regen_attn_desc* desc, regen_block_t* out) {
+    g_last_error.clear();
+    if (!out) return fail(REGEN_ERR_INVALID_ARGUMENT, "out is NULL");
+    *out = nullptr;
+    Problem p;
+    regen_status s = resolve(desc, &p);
+    if (s != REGEN_OK) return s;
+    if (p.flags & (REGEN_ATTN_TOKEN_MAJOR | REGEN_ATTN_PROFILE))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "a block takes no layout or profiling flag");
+    if (p.tokens * int64_t(p.heads) * p.head_dim * 3 * 2 >= (int64_t(1) << 32))
+        return fail(REGEN_ERR_UNSUPPORTED, "the projection output would exceed 4 GiB");
+    regen_block* b = new (std::nothrow) regen_block();
+    if (!b) return fail(REGEN_ERR_OUT_OF_MEMORY, "host allocation of the block failed");
+    s = regen_attn_create(desc, &b->attn);
+    if (s != REGEN_OK) {
+        delete b;
+        return s;
+    }
+    b->N = int(p.tokens);
+    b->hidden = p.heads * p.head_dim;
+    const size_t H = size_t(b->hidden), N = size_t(b->N);
+    hipError_t e;
+    if ((e = hipMalloc(&b->qkv, N * 3 * H * 2)) != hipSuccess ||
+        (e = hipMalloc(&b->attn_out, N * H * 2)) != hipSuccess) {
+        (void)hipGetLastError();
+        block_free(b);
+        return fail(e == hipErrorOutOfMemory ? REGEN_ERR_OUT_OF_MEMORY : REGEN_ERR_HIP,
+                    std::string("device allocation failed: ") + hipGetErrorString(e));
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_blocks_mu);
+        g_blocks.insert(b);
+    }
+    *out = b;
+    return REGEN_OK;
+}
+
+regen_status regen_block_forward(regen_block_t b, const void* x, const void* w_qkv,
+                                 const void* w_o, void* y, void* stream) {
+    g_last_error.clear();
+    if (!b || !block_live(b)) return fail(REGEN_ERR_INVALID_ARGUMENT, "block is NULL or not live");
+    if (!x || !w_qkv || !w_o || !y)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "x, w_qkv, w_o, y must be non-NULL");
+    const uintptr_t ptrs[4] = {uintptr_t(x), uintptr_t(w_qkv), uintptr_t(w_o), uintptr_t(y)};
+    for (uintptr_t a : ptrs)
+        if (a % 16 != 0) return fail(REGEN_ERR_INVALID_ARGUMENT, "x, w_qkv, w_o, y must be 16-byte aligned");
+    const uintptr_t H = uintptr_t(b->hidden), N = uintptr_t(b->N);
+    const uintptr_t xb = N * H * 2, wqb = H * 3 * H * 2, wob = H * H * 2;
+    if (overlaps(ptrs[3], xb, ptrs[0], xb) || overlaps(ptrs[3], xb, ptrs[1], wqb) ||
+        overlaps(ptrs[3], xb, ptrs[2], wob))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "y overlaps x, w_qkv or w_o");
+    int cur = -1;
+    hipError_t ge = hipGetDevice(&cur);
+    if (ge != hipSuccess) return fail_hip(ge, "hipGetDevice");
+    if (cur != b->attn->device)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "the current HIP device is not the block's device");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int Hd = b->hidden;
+    gemm(static_cast<const uint16_t*>(x), Hd, static_cast<const uint16_t*>(w_qkv), Hd, b->qkv, 3 * Hd,
+         b->N, 3 * Hd, Hd, st);
+    const long long D = b->attn->p.head_dim;
+    const Strides sd{D, 3LL * Hd, D, 3LL * Hd, D, Hd};
+    regen_status s = enqueue(b->attn, b->qkv, 0, b->N, b->qkv + Hd, b->qkv + 2 * Hd, 0, b->N,
+                             b->attn_out, nullptr, stream, false, sd);
+    if (s != REGEN_OK) return s;
+    gemm(b->attn_out, Hd, static_cast<const uint16_t*>(w_o), Hd, static_cast<uint16_t*>(y), Hd, b->N,
+         Hd, Hd, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    return REGEN_OK;
+}
+
+regen_status regen_block_destroy(regen_block_t b) {
+    g_last_error.clear();
+    if (!b) return REGEN_OK;
+    {
+        std::lock_guard<std::mutex> lk(g_blocks_mu);
+        if (!g_blocks.erase(b)) return fail(REGEN_ERR_INVALID_ARGUMENT, "block is not live");
+    }
+    block_free(b);
     return REGEN_OK;
 }
 

@@ -29,6 +29,10 @@ EXPORTS = (
     "regen_attn_merge",
     "regen_ulysses_pack",
     "regen_ulysses_unpack",
+    "regen_linear",
+    "regen_block_create",
+    "regen_block_forward",
+    "regen_block_destroy",
     "regen_attn_destroy",
     "regen_attn_status_string",
     "regen_attn_last_error",
@@ -94,6 +98,14 @@ def lib():
         f = getattr(L, name)
         f.argtypes = [vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
         f.restype = ctypes.c_int
+    L.regen_linear.argtypes = [vp, vp, vp, i64, ctypes.c_int, ctypes.c_int, vp]
+    L.regen_linear.restype = ctypes.c_int
+    L.regen_block_create.argtypes = [ctypes.POINTER(regen_attn_desc), ctypes.POINTER(vp)]
+    L.regen_block_create.restype = ctypes.c_int
+    L.regen_block_forward.argtypes = [vp] * 6
+    L.regen_block_forward.restype = ctypes.c_int
+    L.regen_block_destroy.argtypes = [vp]
+    L.regen_block_destroy.restype = ctypes.c_int
     L.regen_attn_destroy.argtypes = [vp]
     L.regen_attn_destroy.restype = ctypes.c_int
     L.regen_attn_status_string.argtypes = [ctypes.c_int]
@@ -160,6 +172,25 @@ def regen_ulysses_pack(x, send, tokens_local, heads, head_dim, groups, stream):
 
 def regen_ulysses_unpack(recv, y, tokens_local, heads, head_dim, groups, stream):
     return lib().regen_ulysses_unpack(recv, y, tokens_local, heads, head_dim, groups, stream)
+
+
+def regen_linear(x, w, y, rows, in_features, out_features, stream):
+    return lib().regen_linear(x, w, y, rows, in_features, out_features, stream)
+
+
+def regen_block_create(desc):
+    """Returns (status, block); block is None on failure."""
+    b = ctypes.c_void_p()
+    s = lib().regen_block_create(ctypes.byref(desc) if desc is not None else None, ctypes.byref(b))
+    return s, (b.value if s == REGEN_OK else None)
+
+
+def regen_block_forward(block, x, w_qkv, w_o, y, stream):
+    return lib().regen_block_forward(block, x, w_qkv, w_o, y, stream)
+
+
+def regen_block_destroy(block):
+    return lib().regen_block_destroy(block)
 
 
 def regen_attn_destroy(handle):
@@ -364,6 +395,74 @@ class Attention:
             self.handle = None
             if s != REGEN_OK:
                 raise RegenAttnError(s, "regen_attn_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def linear(x, w, out=None, stream=None):
+    """y = x w^T for bf16 device tensors x [rows, in], w [out, in]."""
+    import torch
+    rows, fin = (int(a) for a in x.shape)
+    fout = int(w.shape[0])
+    for t, name in ((x, "x"), (w, "w")):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous bf16 device tensor" % name)
+    if tuple(w.shape) != (fout, fin):
+        raise ValueError("w must be [out_features, in_features]")
+    if out is None:
+        out = torch.empty((rows, fout), dtype=torch.bfloat16, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    s = regen_linear(x.data_ptr(), w.data_ptr(), out.data_ptr(), rows, fin, fout, stream.cuda_stream)
+    if s != REGEN_OK:
+        raise RegenAttnError(s, "regen_linear")
+    return out
+
+
+class Block:
+    """Self-attention block [Q|K|V] = X W_qkv, attention, Y = O W_o on the
+    current device; torch supplies memory and the stream only."""
+
+    def __init__(self, heads, head_dim, grid, pairs=(0, 0, 0), rope_base=0.0, sm_scale=0.0,
+                 flags=0):
+        self.heads, self.head_dim, self.grid = int(heads), int(head_dim), tuple(grid)
+        self.hidden = self.heads * self.head_dim
+        self.tokens = self.grid[0] * self.grid[1] * self.grid[2]
+        self.desc = make_desc(heads, head_dim, grid, pairs, rope_base, sm_scale, flags)
+        s, b = regen_block_create(self.desc)
+        if s != REGEN_OK:
+            raise RegenAttnError(s, "regen_block_create")
+        self.handle = b
+
+    def forward(self, x, w_qkv, w_o, out=None, stream=None):
+        import torch
+        shapes = ((x, (self.tokens, self.hidden), "x"), (w_qkv, (3 * self.hidden, self.hidden), "w_qkv"),
+                  (w_o, (self.hidden, self.hidden), "w_o"))
+        for t, shape, name in shapes:
+            if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError("%s must be a contiguous bf16 device tensor of shape %s" % (name, shape))
+        if out is None:
+            out = torch.empty_like(x)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        s = regen_block_forward(self.handle, x.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(),
+                                out.data_ptr(), stream.cuda_stream)
+        if s != REGEN_OK:
+            raise RegenAttnError(s, "regen_block_forward")
+        return out
+
+    __call__ = forward
+
+    def close(self):
+        if self.handle is not None:
+            s = regen_block_destroy(self.handle)
+            self.handle = None
+            if s != REGEN_OK:
+                raise RegenAttnError(s, "regen_block_destroy")
 
     def __del__(self):
         try:

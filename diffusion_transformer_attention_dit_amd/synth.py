@@ -114,6 +114,24 @@ def make_context(w: Workload, ctx_len: int = CONTEXT_TOKENS, step: int = 0, bloc
     return k.to(dtype).contiguous(), v.to(dtype).contiguous()
 
 
+def make_block_inputs(w: Workload, step: int = 0, block: int = 0, device="cpu", base_seed: int = 0,
+                      dtype: torch.dtype = torch.bfloat16):
+    """Synthetic inputs of one self-attention block: hidden states x
+    [T*H*W, heads*head_dim] ~ N(0, 1) and random-init weights in the
+    [out][in] layout of a linear layer, w_qkv [3*hidden, hidden] and w_o
+    [hidden, hidden], ~ N(0, 1/hidden) (no trained weights exist here), from
+    a seed of their own."""
+    hidden = w.heads * w.head_dim
+    n = w.grid[0] * w.grid[1] * w.grid[2]
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_for(w, step, block, base_seed) ^ 0xB10C)
+    x = torch.randn((n, hidden), generator=g, device=device, dtype=torch.float32)
+    sd = hidden ** -0.5
+    w_qkv = torch.randn((3 * hidden, hidden), generator=g, device=device, dtype=torch.float32) * sd
+    w_o = torch.randn((hidden, hidden), generator=g, device=device, dtype=torch.float32) * sd
+    return tuple(t.to(dtype).contiguous() for t in (x, w_qkv, w_o))
+
+
 def sample_rows(n: int, count: int, seed: int, tile: int = 128):
     """A seeded sorted sample of query rows that always holds the first and
     last row and the rows on each side of every `tile` boundary it can fit."""

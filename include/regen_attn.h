@@ -225,6 +225,46 @@ regen_status regen_ulysses_unpack(const void *recv, void *y, int64_t tokens_loca
                                   int head_dim, int groups, void *stream);
 
 /*
+ * A linear layer without bias, y = x w^T: x [rows][in_features], w
+ * [out_features][in_features] (the usual [out][in] weight layout), y
+ * [rows][out_features]; bf16 in and out, fp32 accumulation (MFMA), y
+ * rounded to nearest even. in_features must be a multiple of 64; every
+ * operand under 4 GiB; device pointers, 16-byte aligned, y not overlapping
+ * x or w. Enqueued on `stream` of the current device. Errors:
+ * INVALID_ARGUMENT, UNSUPPORTED (in_features), NO_DEVICE, HIP.
+ */
+regen_status regen_linear(const void *x, const void *w, void *y, int64_t rows, int in_features,
+                          int out_features, void *stream);
+
+/*
+ * One self-attention block of the diffusion transformer around this
+ * attention (index page, "Abstract": the decoder is a DiT; the projection
+ * sizes follow the heads x head_dim of the description, hidden = heads *
+ * head_dim, no biases):
+ *     [Q | K | V] = X W_qkv^T,   O = attention(R Q, R K, V),   Y = O W_o^T.
+ *   x     : [tokens][hidden] bf16, token-major hidden states of the window
+ *   w_qkv : [3 hidden][hidden] bf16 ([out][in]); output rows 0..hidden-1
+ *           give Q, the next hidden give K, the last hidden give V; head h
+ *           uses rows h*head_dim .. h*head_dim + head_dim - 1 of each
+ *   w_o   : [hidden][hidden] bf16 ([out][in])
+ *   y     : [tokens][hidden] bf16 output (must not overlap the inputs)
+ * The projections run as regen_linear; the attention reads Q, K and V in
+ * place out of the projection output (a strided token-major view) and
+ * applies the rotation while loading. All pointers are device memory,
+ * 16-byte aligned, owned by the caller. regen_block_create takes the same
+ * description as regen_attn_create (without REGEN_ATTN_TOKEN_MAJOR or
+ * REGEN_ATTN_PROFILE) and allocates the attention workspace, the projection
+ * output (tokens * 3 hidden bf16) and the attention output (tokens * hidden
+ * bf16); calls on one block must be ordered like calls on one attention
+ * handle. Errors as for the attention calls.
+ */
+typedef struct regen_block *regen_block_t;
+regen_status regen_block_create(const regen_attn_desc *desc, regen_block_t *out);
+regen_status regen_block_forward(regen_block_t b, const void *x, const void *w_qkv,
+                                 const void *w_o, void *y, void *stream);
+regen_status regen_block_destroy(regen_block_t b);
+
+/*
  * Free the handle, its tables and workspace. No call on the handle may still
  * be in flight (the device memory is released immediately). NULL is a no-op
  * returning REGEN_OK; a handle that is not live gives INVALID_ARGUMENT.

@@ -336,9 +336,10 @@ def ulysses_unpack(recv):
 # One self-attention block of the DiT with synthetic weights (index page,
 # "Abstract": the decoder is a diffusion transformer; the blocks' projection
 # sizes are not on the pages and follow the 12 heads x 128 workload):
-#   [Q | K | V] = X W_qkv,  O = attention(R Q, R K, V) per head,  Y = O W_o,
-# X [N, H*d] token-major, W_qkv [H*d, 3*H*d] (columns: Q, then K, then V,
-# head h at columns h*d .. h*d + d - 1 of each), W_o [H*d, H*d], no biases.
+#   [Q | K | V] = X W_qkv^T,  O = attention(R Q, R K, V) per head,  Y = O W_o^T,
+# X [N, H*d] token-major, weights in the [out][in] layout of a linear layer:
+# W_qkv [3*H*d, H*d] (output rows: Q, then K, then V, head h at rows
+# h*d .. h*d + d - 1 of each), W_o [H*d, H*d]; no biases.
 # ---------------------------------------------------------------------------
 
 def block_forward(x, w_qkv, w_o, grid, heads, pairs=None, base=10000.0, scale=None, rows=None):
@@ -346,9 +347,9 @@ def block_forward(x, w_qkv, w_o, grid, heads, pairs=None, base=10000.0, scale=No
     x, w_qkv, w_o = _f64(x), _f64(w_qkv), _f64(w_o)
     n, hidden = x.shape
     d = hidden // heads
-    assert heads * d == hidden and w_qkv.shape == (hidden, 3 * hidden)
+    assert heads * d == hidden and w_qkv.shape == (3 * hidden, hidden)
     assert w_o.shape == (hidden, hidden)
-    qkv = x @ w_qkv  # [N, 3*H*d]
+    qkv = x @ w_qkv.T  # [N, 3*H*d]
 
     def head_major(cols):
         return np.ascontiguousarray(cols.reshape(n, heads, d).transpose(1, 0, 2))
@@ -358,4 +359,4 @@ def block_forward(x, w_qkv, w_o, grid, heads, pairs=None, base=10000.0, scale=No
     v = head_major(qkv[:, 2 * hidden:])
     o = rope_attention(q, k, v, grid, pairs, base, scale, rows=rows)  # [H, R, d]
     o_tok = o.transpose(1, 0, 2).reshape(o.shape[1], hidden)           # [R, H*d]
-    return o_tok @ w_o
+    return o_tok @ w_o.T

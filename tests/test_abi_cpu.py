@@ -148,3 +148,27 @@ def test_merge_argument_checks_before_the_device(kw, expect):
     s = native.regen_attn_merge(parts, lses, kw.get("heads", 2), kw.get("rows", 8),
                                 kw.get("head_dim", 128), kw.get("o", 0x8000000), None, None)
     assert s == expect, native.regen_attn_last_error()
+
+
+def test_block_entry_points_without_device():
+    assert native.regen_block_forward(None, 16, 16, 16, 32, None) == native.REGEN_ERR_INVALID_ARGUMENT
+    assert native.regen_block_destroy(None) == native.REGEN_OK
+    bogus = ctypes.addressof(ctypes.c_int64(0))
+    assert native.regen_block_destroy(bogus) == native.REGEN_ERR_INVALID_ARGUMENT
+    s, b = native.regen_block_create(good_desc(flags=native.REGEN_ATTN_TOKEN_MAJOR))
+    assert s == native.REGEN_ERR_INVALID_ARGUMENT and b is None
+    if not torch.cuda.is_available():
+        s, b = native.regen_block_create(good_desc())
+        assert s == native.REGEN_ERR_NO_DEVICE and b is None
+
+
+def test_linear_argument_checks_before_the_device():
+    E = native.REGEN_ERR_INVALID_ARGUMENT
+    assert native.regen_linear(0, 16, 32, 4, 64, 8, None) == E
+    assert native.regen_linear(16, 32, 48, 0, 64, 8, None) == E
+    assert native.regen_linear(16, 32, 48, 4, 96, 8, None) == native.REGEN_ERR_UNSUPPORTED
+    assert native.regen_linear(16 + 2, 0x100000, 0x200000, 4, 64, 8, None) == E   # misaligned
+    assert native.regen_linear(0x100000, 0x200000, 0x100000, 4, 64, 8, None) == E  # y overlaps x
+    if not torch.cuda.is_available():
+        assert native.regen_linear(0x100000, 0x200000, 0x300000, 4, 64, 8, None) == \
+            native.REGEN_ERR_NO_DEVICE

@@ -501,18 +501,18 @@ def test_ulysses_attention_equals_full_attention():
 def _block_case(heads=2, d=8, grid=(2, 3, 4)):
     n = grid[0] * grid[1] * grid[2]
     x = RNG.standard_normal((n, heads * d))
-    w_qkv = RNG.standard_normal((heads * d, 3 * heads * d)) / math.sqrt(heads * d)
+    w_qkv = RNG.standard_normal((3 * heads * d, heads * d)) / math.sqrt(heads * d)
     w_o = RNG.standard_normal((heads * d, heads * d)) / math.sqrt(heads * d)
     return x, w_qkv, w_o, grid, heads, d
 
 
 def test_block_with_identity_projections_is_attention_of_x():
-    # W_qkv = [I | I | I], W_o = I: the block is attention(x, x, x) laid out
+    # W_qkv = [I; I; I], W_o = I: the block is attention(x, x, x) laid out
     # token-major, which pins the Q/K/V column order and the head layout.
     x, _, _, grid, heads, d = _block_case()
     hid = heads * d
     eye = np.eye(hid)
-    y = oracle.block_forward(x, np.concatenate([eye, eye, eye], axis=1), eye, grid, heads,
+    y = oracle.block_forward(x, np.concatenate([eye, eye, eye], axis=0), eye, grid, heads,
                              pairs=(2, 1, 1))
     xh = x.reshape(-1, heads, d).transpose(1, 0, 2)
     ref = oracle.np_rope_attention(xh, xh, xh, grid, pairs=(2, 1, 1))  # [H, N, d]
@@ -520,18 +520,18 @@ def test_block_with_identity_projections_is_attention_of_x():
 
 
 def test_block_column_roles():
-    # Zeroing the V columns zeroes Y; scaling W_o scales Y; permuting the
-    # columns of W_o permutes the columns of Y.
+    # Zeroing the V rows of W_qkv zeroes Y; scaling W_o scales Y; permuting
+    # the rows of W_o permutes the columns of Y.
     x, w_qkv, w_o, grid, heads, d = _block_case()
     hid = heads * d
     w0 = w_qkv.copy()
-    w0[:, 2 * hid:] = 0.0
+    w0[2 * hid:, :] = 0.0
     assert np.abs(oracle.block_forward(x, w0, w_o, grid, heads, pairs=(2, 1, 1))).max() == 0.0
     y = oracle.block_forward(x, w_qkv, w_o, grid, heads, pairs=(2, 1, 1))
     np.testing.assert_allclose(oracle.block_forward(x, w_qkv, 3.0 * w_o, grid, heads, pairs=(2, 1, 1)),
                                3.0 * y, rtol=1e-13, atol=1e-14)
     perm = RNG.permutation(hid)
-    np.testing.assert_allclose(oracle.block_forward(x, w_qkv, w_o[:, perm], grid, heads,
+    np.testing.assert_allclose(oracle.block_forward(x, w_qkv, w_o[perm, :], grid, heads,
                                                     pairs=(2, 1, 1)), y[:, perm], rtol=0, atol=1e-14)
 
 
@@ -542,7 +542,7 @@ def test_block_pure_python_brute_force():
     n, hid = x.shape
     y = oracle.block_forward(x, w_qkv, w_o, grid, heads)
     P = (1, 1, 1)  # the default split at d = 6
-    qkv = [[sum(x[i][c] * w_qkv[c][j] for c in range(hid)) for j in range(3 * hid)] for i in range(n)]
+    qkv = [[sum(x[i][c] * w_qkv[j][c] for c in range(hid)) for j in range(3 * hid)] for i in range(n)]
     coords = [(i // (grid[1] * grid[2]), (i // grid[2]) % grid[1], i % grid[2]) for i in range(n)]
 
     def rot(vec, pos):
@@ -569,5 +569,5 @@ def test_block_pure_python_brute_force():
             z = sum(e)
             for c in range(d):
                 o[i][h * d + c] = sum(e[j] * qkv[j][2 * hid + h * d + c] for j in range(n)) / z
-    ref = [[sum(o[i][c] * w_o[c][j] for c in range(hid)) for j in range(hid)] for i in range(n)]
+    ref = [[sum(o[i][c] * w_o[j][c] for c in range(hid)) for j in range(hid)] for i in range(n)]
     np.testing.assert_allclose(y, np.array(ref), rtol=0, atol=1e-12)
