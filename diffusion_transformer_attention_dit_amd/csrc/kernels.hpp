@@ -117,15 +117,27 @@ __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     const int n0 = tile * kPrepKeys;
     const int HW = geo.H * geo.W;
 
-    for (int cid = threadIdx.x; cid < kPrepKeys * CPR; cid += 256) {
-        const int r = cid / CPR, c = cid % CPR;
-        const int n = n0 + r;
+    // K: every thread rotates PER chunks (one 16-byte column chunk c of PER
+    // rows); all loads are issued before the first rotation.
+    constexpr int PER = kPrepKeys * CPR / 256;
+    static_assert(PER * 256 == kPrepKeys * CPR, "chunks per thread");
+    uint4 kin[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int cid = threadIdx.x + i * 256;
+        const int n = n0 + cid / CPR, c = cid % CPR;
+        kin[i] = make_uint4(0, 0, 0, 0);
+        if (n < N) kin[i] = *reinterpret_cast<const uint4*>(k + hd * sh + n * sn + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int cid = threadIdx.x + i * 256;
+        const int n = n0 + cid / CPR, c = cid % CPR;
         uint4 out = make_uint4(0, 0, 0, 0);
         if (n < N) {
-            uint4 in = *reinterpret_cast<const uint4*>(k + hd * sh + n * sn + c * 8);
             const int ng = n_off + n;  // token index on the grid
             const int t = ng / HW, h = (ng / geo.W) % geo.H, w = ng % geo.W;
-            out = rope_chunk(in, tab, geo, c * 4, t, h, w);
+            out = rope_chunk(kin[i], tab, geo, c * 4, t, h, w);
         }
         *reinterpret_cast<uint4*>(kr + ((size_t)hd * Npad + n) * D + c * 8) = out;
     }
@@ -307,7 +319,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, float* __restrict__ lse,
     const float2* __restrict__ tab, RopeGeom geo, int Nq, int Nk, int Npad, int q_off,
     long long qh, long long qn_stride, long long oh, long long on_stride, Sched sc,
-    float c2 /* sm_scale * log2(e) */, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float c2 /* sm_scale * log2(e) */, int rotate_q, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(BN == 64 || BN == 128, "key tile");
     constexpr int BM = NW * 32;
@@ -367,7 +380,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 uint4 x = make_uint4(0, 0, 0, 0);
                 if (qrow < Nq) {
                     x = *reinterpret_cast<const uint4*>(qp + kb * 16);
-                    x = rope_chunk(x, tab, geo, kb * 8 + half * 4, tt, hh, ww, c2);
+                    if (rotate_q) {
+                        x = rope_chunk(x, tab, geo, kb * 8 + half * 4, tt, hh, ww, c2);
+                    } else {  // unrotated (cross-attention): scale and round only
+                        const uint32_t src[4] = {x.x, x.y, x.z, x.w};
+                        uint32_t dst[4];
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) dst[p] = pack_bf16(bf_lo(src[p]) * c2, bf_hi(src[p]) * c2);
+                        x = make_uint4(dst[0], dst[1], dst[2], dst[3]);
+                    }
                 }
                 qf[kb] = __builtin_bit_cast(bf16x8, x);
             }

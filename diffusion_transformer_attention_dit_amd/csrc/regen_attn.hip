@@ -396,7 +396,7 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<128, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
                            st, q16, h->d_kr, h->d_vt, o16, lse, tab, h->geo, Nq, Nk, Npad,
-                           q_off, qh, qn, oh, on, sc, c2, h->d_part_o, h->d_part_ml);
+                           q_off, qh, qn, oh, on, sc, c2, int(!cross), h->d_part_o, h->d_part_ml);
         mark(2);
         if (rem_tiles > 0)
             hipLaunchKernelGGL((regen::merge_kernel<128, kNW>), mgrid, dim3(256), 0, st, o16, lse,
@@ -407,7 +407,7 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<64, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
                            st, q16, h->d_kr, h->d_vt, o16, lse, tab, h->geo, Nq, Nk, Npad,
-                           q_off, qh, qn, oh, on, sc, c2, h->d_part_o, h->d_part_ml);
+                           q_off, qh, qn, oh, on, sc, c2, int(!cross), h->d_part_o, h->d_part_ml);
         mark(2);
         if (rem_tiles > 0)
             hipLaunchKernelGGL((regen::merge_kernel<64, kNW>), mgrid, dim3(256), 0, st, o16, lse,
