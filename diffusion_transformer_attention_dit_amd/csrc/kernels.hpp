@@ -3,9 +3,11 @@
 // Two kernels make one attention call:
 //
 //  1. rope_k_vt_kernel (HBM-bound pass over K and V): applies the 3D rotary
-//     embedding to K and rounds it to bf16 into a padded row-major copy Kr,
-//     and writes V transposed into Vt, a key-contiguous layout that the P V
-//     matrix product can feed straight from LDS as MFMA operands.
+//     embedding to K and rounds it to bf16 into Kr, and writes V transposed
+//     into Vt. Both are stored as the MFMA operand fragments the attention
+//     kernel reads, in lane order, so that a tile is copied to LDS as
+//     contiguous 1 KiB runs and every operand read is one LDS address plus a
+//     constant.
 //  2. attn_fwd_kernel (MFMA-bound): flash-style exact attention, persistent
 //     (one round of resident workgroups, see Sched). Each wave owns 32 query
 //     rows, rotates its Q rows while loading them (RoPE on load), then
@@ -45,8 +47,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kPrepKeys = 128;  // keys per rope_k_vt block; workspace padding unit
-constexpr int kVtBlk = 64;      // key slots per Vt block
+constexpr int kPrepKeys = 128;  // workspace padding unit (keys)
+constexpr int kPrepBlock = 64;  // keys per rope_k_vt block: one Kr / Vt tile
 
 // Rotary geometry: latent grid, pairs per axis, offsets of each axis' table
 // in the (cos, sin) table. Entry off[a] + pos * pairs[a] + j holds
@@ -99,77 +101,95 @@ __device__ __forceinline__ uint4 rope_chunk(uint4 in, const float2* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: K rotation + V transpose. Grid (Npad / 128, heads), 256 threads.
+// Kernel 1: K rotation + V transpose. Grid (Npad / 64, heads), 256 threads.
 //   k, v : bf16, key n of head h at element h * sh + n * sn (head-major
 //          [heads][N][D]: sh = N D, sn = D; token-major [N][heads][D]:
 //          sh = D, sn = heads D), key n being token n_off + n of the grid.
-//   Kr : [heads][Npad][D] bf16, rotated, rows >= N zero.
-//   Vt : [heads][Npad/64][D][64] bf16; inside each group of 16 slots, slot
-//        8g + j holds key 8(j/4) + 4g + j%4 of that group; keys >= N zero.
+//   Kr, Vt : [heads][Npad/64] tiles of 64 keys, 64 D bf16 each, a tile
+//        being a run of 1 KiB MFMA A-operand fragments; lane l = 32 g + c of
+//        a fragment holds bytes 16 l .. 16 l + 15:
+//        Kr fragment f = 2 kb + kk: key 32 kk + c of the tile, head dims
+//          16 kb + 8 g .. + 7, rotated;
+//        Vt fragment 4 db + kq: head dim 32 db + c of the 8 keys in slots
+//          8 g .. 8 g + 7 of the tile's key group kq (16 keys), slot 8 g + j
+//          holding key 8 (j / 4) + 4 g + j % 4 of the group.
+//        Keys >= N are zero.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ kr,
     uint16_t* __restrict__ vt, const float2* __restrict__ tab, RopeGeom geo, int N, int Npad,
     int n_off, long long sh, long long sn) {
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
-    const int tile = blockIdx.x, hd = blockIdx.y;
-    const int n0 = tile * kPrepKeys;
+    const int hd = blockIdx.y;
+    const int n0 = blockIdx.x * kPrepBlock;
     const int HW = geo.H * geo.W;
 
-    // K: every thread rotates PER chunks (one 16-byte column chunk c of PER
-    // rows); all loads are issued before the first rotation.
-    constexpr int PER = kPrepKeys * CPR / 256;
-    static_assert(PER * 256 == kPrepKeys * CPR, "chunks per thread");
-    uint4 kin[PER];
+    // Rows are staged through LDS so that both the reads of K and V (whole
+    // rows) and the writes of Kr and Vt (whole 1 KiB fragments) are
+    // contiguous. LDS rows are XOR-swizzled by 16-byte chunk.
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int PER = kPrepBlock * CPR / 256;
+    constexpr int NK = D / 8;              // 1 KiB fragments per 64-key Kr tile
+    constexpr int NV = (D / 32) * 4;       // 1 KiB fragments per 64-key Vt tile
+    static_assert(NK * 64 == PER * 256 && NV * 64 == PER * 256, "fragments per block");
+    __shared__ uint4 kl[kPrepBlock * CPR];
+    __shared__ uint4 vl[kPrepBlock * CPR];
+    const int tid = threadIdx.x;
+    auto sw = [](int r, int c) { return r * CPR + (c ^ (r & (CPR - 1))); };
+
+    uint4 kin[PER], vin[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int cid = threadIdx.x + i * 256;
-        const int n = n0 + cid / CPR, c = cid % CPR;
+        const int cid = i * 256 + tid, r = cid / CPR, c = cid % CPR, n = n0 + r;
         kin[i] = make_uint4(0, 0, 0, 0);
-        if (n < N) kin[i] = *reinterpret_cast<const uint4*>(k + hd * sh + n * sn + c * 8);
+        vin[i] = make_uint4(0, 0, 0, 0);
+        if (n < N) {
+            kin[i] = *reinterpret_cast<const uint4*>(k + hd * sh + n * sn + c * 8);
+            vin[i] = *reinterpret_cast<const uint4*>(v + hd * sh + n * sn + c * 8);
+        }
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int cid = threadIdx.x + i * 256;
-        const int n = n0 + cid / CPR, c = cid % CPR;
+        const int cid = i * 256 + tid, r = cid / CPR, c = cid % CPR, n = n0 + r;
         uint4 out = make_uint4(0, 0, 0, 0);
         if (n < N) {
             const int ng = n_off + n;  // token index on the grid
             const int t = ng / HW, h = (ng / geo.W) % geo.H, w = ng % geo.W;
             out = rope_chunk(kin[i], tab, geo, c * 4, t, h, w);
         }
-        *reinterpret_cast<uint4*>(kr + ((size_t)hd * Npad + n) * D + c * 8) = out;
+        kl[sw(r, c)] = out;
+        vl[sw(r, c)] = vin[i];
     }
+    __syncthreads();
 
-    // V: each thread gathers the 8 keys of one 8-slot output chunk for one
-    // column chunk of 8 head dims, transposes the 8 x 8 block in registers
-    // and writes 8 rows of 16 bytes. Threads with consecutive g write one
-    // 128-byte Vt row together.
-    constexpr int COMBOS = 16 * CPR;
-    const int tid = threadIdx.x;
-    if (tid < COMBOS) {
-        const int g = tid % 8, rest = tid / 8;
-        const int blk = rest % 2, c = rest / 2;
-        const int G = blk * 4 + g / 2, hh = g % 2;
-        uint32_t a[8][4];
+    // Fragment F = tile * NK + f of Kr (f = 2 kb + kk): lane (c, g) holds key
+    // 32 kk + c, head dims 16 kb + 8 g .. + 7. Fragment F = tile * NV + gp of
+    // Vt (gp = 4 db + kq): lane (c, g) holds head dim 32 db + c of the keys
+    // in slots 8 g .. 8 g + 7 of key group kq.
+    const int lane = tid & 63, c = lane & 31, g = lane >> 5;
+    uint16_t* kdst = kr + ((size_t)hd * Npad + n0) * D;
+    uint16_t* vdst = vt + ((size_t)hd * Npad + n0) * D;
+    const uint16_t* vl16 = reinterpret_cast<const uint16_t*>(vl);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int key = n0 + G * 16 + (j / 4) * 8 + hh * 4 + (j % 4);
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (key < N) x = *reinterpret_cast<const uint4*>(v + hd * sh + key * sn + c * 8);
-            a[j][0] = x.x; a[j][1] = x.y; a[j][2] = x.z; a[j][3] = x.w;
+    for (int i = 0; i < PER; ++i) {
+        const int F = i * 4 + (tid >> 6);
+        {
+            const int tl = F / NK, f = F % NK;
+            const int r = tl * 64 + (f % 2) * 32 + c;
+            *reinterpret_cast<uint4*>(kdst + F * 512 + lane * 8) = kl[sw(r, (f / 2) * 2 + g)];
         }
-        uint16_t* dst = vt + ((size_t)(hd * (Npad / kVtBlk) + tile * 2 + blk) * D + c * 8) * kVtBlk + g * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            uint32_t wv[4];
+        {
+            const int tl = F / NV, gp = F % NV, d = (gp / 4) * 32 + c;
+            const int rb = tl * 64 + (gp % 4) * 16 + 4 * g;
+            uint32_t w4[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                uint32_t x0 = a[2 * m][e / 2], x1 = a[2 * m + 1][e / 2];
-                wv[m] = (e & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+                const int r0 = rb + (m / 2) * 8 + (m % 2) * 2, r1 = r0 + 1;
+                const uint32_t lo = vl16[sw(r0, d >> 3) * 8 + (d & 7)];
+                const uint32_t hi = vl16[sw(r1, d >> 3) * 8 + (d & 7)];
+                w4[m] = lo | (hi << 16);
             }
-            *reinterpret_cast<uint4*>(dst + e * kVtBlk) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            *reinterpret_cast<uint4*>(vdst + F * 512 + lane * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
         }
     }
 }
@@ -212,32 +232,24 @@ __device__ __forceinline__ void g2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voff
                                              16, voff, 0, 0, 0);
 }
 
-// Issue the copies of K tile j (BN rows of Kr) and its Vt slots into LDS
-// buffer (ks, vs). Every wave copies whole 1 KiB runs of the swizzled
-// tiles; lane l of a run at tile position p fetches the logical chunk that
-// the swizzle places at p.
+// Issue the copies of K tile j and Vt tile j into LDS buffer (ks, vs). Both
+// are stored in HBM as runs of 1 KiB MFMA operand fragments in lane order,
+// which land unchanged in LDS: run r of a tile goes to byte 1024 r of the
+// buffer, every wave copying RUNS / NW whole runs of each.
 template <int D, int BN, int NW>
 __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                            int j, char* ks, char* vs, int wave, int lane) {
-    constexpr int KRB = D * 2, VRB = BN * 2;  // LDS row bytes
-    constexpr int RUNS = BN * D * 2 / 1024;   // 1 KiB runs per tile (same for K and V)
+    constexpr int RUNS = BN * D * 2 / 1024;  // 1 KiB runs per tile (same for K and V)
     static_assert(RUNS % NW == 0, "runs per wave");
+    const uint32_t tile_off = (uint32_t)j * (RUNS * 1024);
 #pragma unroll
     for (int i = 0; i < RUNS / NW; ++i) {
         const int run = i * NW + wave;
-        const int p = run * 64 + lane;  // chunk position in the tile
-        {
-            const int r = p / (KRB / 16), pc = p % (KRB / 16);
-            const int c = (KRB == 256) ? (pc ^ (r & 15)) : (pc ^ ((r >> 1) & 7));
-            g2lds16(krs, (uint32_t)((j * BN + r) * D * 2 + c * 16), ks + run * 1024);
-        }
-        {
-            const int d = p / (VRB / 16), pc = p % (VRB / 16);
-            const int c = (VRB == 256) ? (pc ^ (d & 15)) : (pc ^ ((d >> 1) & 7));
-            const int blk = c / 8, g = c % 8;
-            g2lds16(vrs, (uint32_t)((((j * BN / kVtBlk + blk) * D + d) * kVtBlk + g * 8) * 2),
-                    vs + run * 1024);
-        }
+        const uint32_t voff = (uint32_t)(run * 1024 + lane * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            krs, (__attribute__((address_space(3))) void*)(ks + run * 1024), 16, voff, tile_off, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vrs, (__attribute__((address_space(3))) void*)(vs + run * 1024), 16, voff, tile_off, 0, 0);
     }
 }
 
@@ -322,16 +334,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     float c2 /* sm_scale * log2(e) */, int rotate_q, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
     static_assert(D == 64 || D == 128, "head_dim");
-    static_assert(BN == 64 || BN == 128, "key tile");
+    static_assert(BN == 64, "key tile: the Kr / Vt fragment layout holds 64-key tiles");
     constexpr int BM = NW * 32;
-    constexpr int KRB = D * 2, VRB = BN * 2;  // LDS row bytes of the K and Vt tiles
-    constexpr int KBYTES = BN * KRB, VBYTES = D * VRB;
+    constexpr int KBYTES = BN * D * 2, VBYTES = D * BN * 2;  // LDS bytes of a K / Vt tile
     constexpr float kLazy = 8.0f;  // rescale only when the max grows by > 2^8
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * (KBYTES + VBYTES)];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
 
     // Consecutive logical workgroups (hence consecutive tiles of one head)
@@ -415,7 +426,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
         for (int b = kv0; b < kv1; ++b) {
             const char* ks = smem + buf * (KBYTES + VBYTES);
-            const char* vs = ks + KBYTES;
             {
                 char* nks = smem + (buf ^ 1) * (KBYTES + VBYTES);
                 if (b + 1 < kv1)
@@ -425,22 +435,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
 
             // MFMA A operands come from LDS through a ring of RING fragments
-            // read ahead of their use: fragments 0..NK-1 are the K tile (head-
-            // dim block kb major, key block kk minor, so consecutive S MFMAs
-            // feed different accumulators), NK..NK+NV-1 the Vt tile (head-dim
-            // block db, key block kq). LDS read bandwidth is close to what the
+            // read ahead of their use; fragment f sits at byte 1024 f of the
+            // buffer, lane l's part at 16 l. Fragments 0..NK-1 are the K tile
+            // (head-dim block kb major, key block kk minor, so consecutive S
+            // MFMAs feed different accumulators), NK..NK+NV-1 the Vt tile
+            // (head-dim block db, key block kq). LDS read bandwidth is close to what the
             // S products need while all waves run them at once, so the first
             // Vt fragments are requested after the S products, to land during
             // the softmax.
             constexpr int KB = D / 16, NK = (BN / 32) * KB, QB16 = BN / 16, NV = (D / 32) * QB16;
             constexpr int RING = 8;
             auto frag = [&](int f) -> bf16x8 {
-                if (f < NK) {
-                    const int kk = f % (BN / 32), kb = f / (BN / 32);
-                    return *reinterpret_cast<const bf16x8*>(ks + swz_off<KRB>(kk * 32 + col, kb * 2 + half));
-                }
-                const int g = f - NK, db = g / QB16, kq = g % QB16;
-                return *reinterpret_cast<const bf16x8*>(vs + swz_off<VRB>(db * 32 + col, kq * 2 + half));
+                return *reinterpret_cast<const bf16x8*>(ks + f * 1024 + lane * 16);
             };
             bf16x8 fr[RING];
 #pragma unroll
@@ -480,12 +486,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int kk = 0; kk < BN / 32; ++kk)
 #pragma unroll
-                for (int i = (kk == 0 ? 4 : 0); i < 16; ++i) mp[i & 3] = fmaxf(mp[i & 3], s[kk][i]);
-            float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+                for (int i = (kk == 0 ? 4 : 0); i < 16; ++i) mp[i & 3] = __builtin_elementwise_maximum(mp[i & 3], s[kk][i]);
+            float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mp[0], mp[1]),
+                                                     __builtin_elementwise_maximum(mp[2], mp[3]));
             {
                 auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                            false, false);
-                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+                mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
             // Lazy rescale: keep the reference m_run unless the row max passes
             // it by more than kLazy, so P = exp2(s) stays <= 2^kLazy; the final

@@ -349,7 +349,7 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
     const int Npad = int((nk + regen::kPrepKeys - 1) / regen::kPrepKeys * regen::kPrepKeys);
     const float c2 = p.scale * 1.4426950408889634f;
 
-    dim3 pgrid(unsigned(Npad / regen::kPrepKeys), unsigned(p.heads));
+    dim3 pgrid(unsigned(Npad / regen::kPrepBlock), unsigned(p.heads));
     regen::Sched sc;
     sc.n_qtiles = int((nq + kBM - 1) / kBM);
     sc.nkv = int((nk + kBN - 1) / kBN);
