@@ -340,6 +340,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     constexpr float kLazy = 8.0f;  // rescale only when the max grows by > 2^8
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * (KBYTES + VBYTES)];
+    // The next segment's Q rows, copied during the current segment: row r at
+    // byte r * 2 D, 16-byte chunk c stored at position c ^ (r % (D / 8)).
+    __shared__ __attribute__((aligned(1024))) char qsm[BM * D * 2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -361,6 +364,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         *krs = make_rsrc(kr + (size_t)h * Npad * D, head_bytes);
         *vrs = make_rsrc(vt + (size_t)h * Npad * D, head_bytes);
     };
+    // Copies of the BM Q rows of tile tt into qsm (this wave's share of the
+    // 1 KiB runs). The resource covers the tile's rows below Nq only, so
+    // rows past the end read as zero. Used when a tile's rows span < 2^31
+    // bytes (uniform).
+    constexpr int QCPR = D / 8;  // 16-byte chunks per Q row
+    const bool q_lds = (long long)qn_stride * 2 * BM < (1LL << 31);
+    auto issue_q = [&](long long tt) {
+        const int h = (int)tt / sc.n_qtiles, qtt = (int)tt - h * sc.n_qtiles;
+        const int rows = min(BM, Nq - qtt * BM);
+        const __amdgpu_buffer_rsrc_t qrs =
+            make_rsrc(q + h * qh + (long long)qtt * BM * qn_stride,
+                      (uint32_t)(((long long)(rows - 1) * qn_stride + D) * 2));
+        constexpr int RUNS = BM * D * 2 / 1024;
+        static_assert(RUNS % NW == 0, "Q runs per wave");
+#pragma unroll
+        for (int i = 0; i < RUNS / NW; ++i) {
+            const int run = i * NW + wave;
+            const int p = run * 64 + lane;  // chunk position in qsm
+            const int r = p / QCPR, c = (p % QCPR) ^ (r % QCPR);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                qrs, (__attribute__((address_space(3))) void*)(qsm + run * 1024), 16,
+                (uint32_t)(((long long)r * qn_stride + c * 8) * 2), 0, 0, 0);
+        }
+    };
+
     __amdgpu_buffer_rsrc_t krs, vrs;
     head_rsrc(t, &krs, &vrs);
     issue_tile<D, BN, NW>(krs, vrs, kv0, smem, smem + KBYTES, wave, lane);
@@ -386,11 +414,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             const int qg = q_off + qn;  // token index on the grid
             const int tt = qg / HW, hh = (qg / geo.W) % geo.H, ww = qg % geo.W;
             const uint16_t* qp = q + hd * qh + qn * qn_stride + half * 8;
+            // From LDS when the previous segment prefetched this tile's rows.
+            const bool from_lds = q_lds && k > 0;
+            const int lr = wave * 32 + col;
 #pragma unroll
             for (int kb = 0; kb < D / 16; ++kb) {
                 uint4 x = make_uint4(0, 0, 0, 0);
                 if (qrow < Nq) {
-                    x = *reinterpret_cast<const uint4*>(qp + kb * 16);
+                    if (from_lds)
+                        x = *reinterpret_cast<const uint4*>(qsm + lr * D * 2 + ((kb * 2 + half) ^ (lr % QCPR)) * 16);
+                    else
+                        x = *reinterpret_cast<const uint4*>(qp + kb * 16);
                     if (rotate_q) {
                         x = rope_chunk(x, tab, geo, kb * 8 + half * 4, tt, hh, ww, c2);
                     } else {  // unrotated (cross-attention): scale and round only
@@ -426,6 +460,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
         for (int b = kv0; b < kv1; ++b) {
             const char* ks = smem + buf * (KBYTES + VBYTES);
+            // The next segment's Q rows, once every wave has read this
+            // segment's (the first block's barrier); they land with this
+            // block's copies.
+            if (q_lds && more && b == kv0 + 1) issue_q(nt_);
             {
                 char* nks = smem + (buf ^ 1) * (KBYTES + VBYTES);
                 if (b + 1 < kv1)
@@ -554,6 +592,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             buf ^= 1;
+        }
+
+        if (q_lds && more && kv1 - kv0 == 1) {
+            // A one-block segment: copy the next Q rows now and wait.
+            issue_q(nt_);
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
         }
 
         // ---- segment epilogue ----

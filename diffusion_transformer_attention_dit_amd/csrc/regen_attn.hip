@@ -87,6 +87,11 @@ regen_status resolve(const regen_attn_desc* d, Problem* p) {
         return fail(REGEN_ERR_INVALID_ARGUMENT, "tensor too large");
     if (d->head_dim != 64 && d->head_dim != 128)
         return fail(REGEN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    // One head's rotated K (and transposed V) is addressed through a buffer
+    // resource with 32-bit offsets.
+    if ((tokens + regen::kPrepKeys - 1) / regen::kPrepKeys * regen::kPrepKeys * d->head_dim * 2 >=
+        (int64_t(1) << 31))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "too many tokens for one head (K workspace >= 2^31 bytes)");
     p->heads = d->heads;
     p->head_dim = d->head_dim;
     p->T = d->grid_t;

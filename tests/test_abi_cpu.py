@@ -81,6 +81,18 @@ def test_create_rejects_bad_descriptions(mutate, expect):
     assert native.regen_attn_workspace_size(d) == 0
 
 
+def test_one_head_key_workspace_limit():
+    # 2^31 bytes of rotated K for one head is one past the limit; just below
+    # it the description is valid (its workspace size is reported).
+    over = good_desc(heads=1, grid=(128, 256, 256))  # 8388608 tokens x 128 x 2 B = 2^31
+    assert native.regen_attn_workspace_size(over) == 0
+    s, h = native.regen_attn_create(over)
+    assert s == native.REGEN_ERR_INVALID_ARGUMENT and h is None
+    assert "one head" in native.regen_attn_last_error()
+    under = good_desc(heads=1, grid=(127, 256, 256))
+    assert native.regen_attn_workspace_size(under) == 2 * 127 * 256 * 256 * 128 * 2
+
+
 def test_create_rejects_null_desc():
     s, h = native.regen_attn_create(None)
     assert s == native.REGEN_ERR_INVALID_ARGUMENT and h is None
