@@ -650,11 +650,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 3: merge of split leftover tiles. Grid (rem tiles, BM / 4): one
-// wave per query row, D/64 head dims per lane. A tile held whole by one
+// Kernel 3: merge of split leftover tiles. Grid (rem tiles, BM): one block of
+// 4 waves per query row, D/64 head dims per lane. A tile held whole by one
 // workgroup returns at once. For row r over the segments s holding it:
 //   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 //   lse = ln 2 (M + log2 sum_s 2^(m_s - M) l_s).
+// Wave w folds segments w, w + 4, ... in one pass with a running maximum; the
+// four partial results are then folded the same way.
 // ---------------------------------------------------------------------------
 template <int D, int NW>
 __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -663,50 +665,75 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
                                                     Sched sc, long long oh, long long on_stride) {
     constexpr int BM = NW * 32;
     constexpr int DPL = D / 64;  // head dims per lane (2 or 1)
+    constexpr int MW = 4;        // waves per row
     const long long t = (long long)sc.full * sc.P + blockIdx.x;
     const long long y0 = (long long)blockIdx.x * sc.nkv;  // leftover unit offsets of tile t
     const int p0 = rem_owner(sc, y0);
     const int p1 = rem_owner(sc, y0 + sc.nkv - 1);
     if (p0 == p1) return;  // uniform over the block
     const int hd = (int)(t / sc.n_qtiles), qt = (int)(t % sc.n_qtiles);
-    const int r = blockIdx.y * 4 + (int)(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.y;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int qrow = qt * BM + r;
-    if (qrow >= N) return;  // uniform over the wave
+    if (qrow >= N) return;  // uniform over the block
 
     // Partial slots: every workgroup after p0 starts its range inside tile
     // t, so t is its first leftover tile (slot 2p); p0's range starts in t
     // only if its first unit is t's first unit.
     const int slot0 = partial_slot(sc, p0, t);
-    auto slot_of = [&](int p) { return p == p0 ? slot0 : 2 * p; };
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int p = p0; p <= p1; ++p) M = fmaxf(M, part_ml[((size_t)slot_of(p) * BM + r) * 2]);
-    float L = 0.0f, acc[DPL];
+    float M = -INFINITY, L = 0.0f, acc[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
-#pragma unroll 8
-    for (int p = p0; p <= p1; ++p) {
-        const int slot = slot_of(p);
+#pragma unroll 4
+    for (int p = p0 + w; p <= p1; p += MW) {
+        const int slot = p == p0 ? slot0 : 2 * p;
         const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((size_t)slot * BM + r) * 2);
-        const float w = __builtin_amdgcn_exp2f(ml.x - M);
-        L += w * ml.y;
         const float* po = part_o + ((size_t)slot * BM + r) * D + lane * DPL;
+        float x[DPL];
         if constexpr (DPL == 2) {
-            const float2 x = *reinterpret_cast<const float2*>(po);
-            acc[0] += w * x.x;
-            acc[1] += w * x.y;
+            const float2 v = *reinterpret_cast<const float2*>(po);
+            x[0] = v.x;
+            x[1] = v.y;
         } else {
-            acc[0] += w * po[0];
+            x[0] = po[0];
         }
+        const float Mn = fmaxf(M, ml.x);
+        const float a = __builtin_amdgcn_exp2f(M - Mn), b = __builtin_amdgcn_exp2f(ml.x - Mn);
+        L = L * a + b * ml.y;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * a + b * x[i];
+        M = Mn;
     }
-    const float inv = 1.0f / L;
-    if (lse != nullptr && lane == 0) lse[(size_t)hd * N + qrow] = (M + log2f(L)) * 0.69314718055994531f;
+    __shared__ float sm_ml[MW][2];
+    __shared__ float sm_o[MW][D];
+    if (lane == 0) {
+        sm_ml[w][0] = M;
+        sm_ml[w][1] = L;
+    }
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) sm_o[w][lane * DPL + i] = acc[i];
+    __syncthreads();
+    if (w != 0) return;
+    float Mt = sm_ml[0][0];
+#pragma unroll
+    for (int v = 1; v < MW; ++v) Mt = fmaxf(Mt, sm_ml[v][0]);
+    float Lt = 0.0f, at[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) at[i] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < MW; ++v) {
+        const float b = __builtin_amdgcn_exp2f(sm_ml[v][0] - Mt);  // 0 for a wave with no segment
+        Lt += b * sm_ml[v][1];
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) at[i] += b * sm_o[v][lane * DPL + i];
+    }
+    const float inv = 1.0f / Lt;
+    if (lse != nullptr && lane == 0) lse[(size_t)hd * N + qrow] = (Mt + log2f(Lt)) * 0.69314718055994531f;
     uint16_t* op = o + hd * oh + qrow * on_stride + lane * DPL;
     if constexpr (DPL == 2) {
-        *reinterpret_cast<uint32_t*>(op) = pack_bf16(acc[0] * inv, acc[1] * inv);
+        *reinterpret_cast<uint32_t*>(op) = pack_bf16(at[0] * inv, at[1] * inv);
     } else {
-        const uint32_t w2 = pack_bf16(acc[0] * inv, 0.0f);
+        const uint32_t w2 = pack_bf16(at[0] * inv, 0.0f);
         *op = (uint16_t)(w2 & 0xffffu);
     }
 }

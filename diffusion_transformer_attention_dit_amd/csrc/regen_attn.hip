@@ -364,7 +364,7 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
     const int64_t rem_tiles = tiles - int64_t(sc.full) * h->P;
     sc.rem_units = rem_tiles * sc.nkv;
     sc.Prem = int(sc.rem_units < h->P ? (sc.rem_units > 0 ? sc.rem_units : 1) : h->P);
-    const dim3 mgrid{unsigned(rem_tiles), unsigned(kBM / 4), 1u};
+    const dim3 mgrid{unsigned(rem_tiles), unsigned(kBM), 1u};
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
     const uint16_t* k16 = static_cast<const uint16_t*>(k);
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
