@@ -47,6 +47,10 @@ def parse():
                     help="skip the attention-block leg (profiling runs of the window alone)")
     ap.add_argument("--block-only", action="store_true",
                     help="run only the attention-block leg and print it")
+    ap.add_argument("--no-clip", action="store_true",
+                    help="skip the 77-frame clip leg (profiling runs of the window alone)")
+    ap.add_argument("--clip-only", action="store_true",
+                    help="run only the 77-frame clip leg and print it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run 3 device-to-device copies of this many MiB (to scale HBM "
                          "byte counters against a copy of known size) and exit")
@@ -267,6 +271,43 @@ def cross_leg(w, reps=20):
     return out
 
 
+def clip_leg(reps=6, sets=2):
+    """The 77-frame clip window's attention (12 heads x 31200 tokens x 128, per-head scale
+    U(0.25, 1)): per-call time of the same library calls over `sets` seeded input sets, with the
+    attention kernel's own duration from the library's kernel events; the window time is 120 x
+    the per-call time (extrapolated, labelled so)."""
+    import torch
+
+    from diffusion_transformer_attention_dit_amd import native, synth
+    c = synth.WORKLOADS["clip77_12x128_n31200"]
+    stream = torch.cuda.current_stream()
+    inputs = [synth.make_qkv(c, 0, b, device="cuda") for b in range(sets)]
+    o = torch.empty_like(inputs[0][0])
+    attn = native.Attention(c.heads, c.head_dim, c.grid, flags=native.REGEN_ATTN_PROFILE)
+    attn.forward(*inputs[0], out=o, stream=stream)
+    torch.cuda.synchronize()
+    attn.profile_read()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for r in range(reps):
+        attn.forward(*inputs[r % sets], out=o, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    t_call = a.elapsed_time(b) / reps * 1e-3
+    prep_ms, attn_ms, merge_ms, n = attn.profile_read()
+    attn.close()
+    t_attn = attn_ms / n * 1e-3
+    return {"workload": c.name, "calls_timed": reps,
+            "ms_per_call": round(t_call * 1e3, 3),
+            "tflops_per_call": round(c.flops_per_call / t_call / 1e12, 2),
+            "ms_per_window_extrapolated": round(t_call * 1e3 * c.calls, 1),
+            "attention_kernel": {"kernel": "attn_fwd_kernel", "avg_launch_us": round(t_attn * 1e6, 1),
+                                 "bound": "mfma", "achieved": round(c.flops_per_call / t_attn / 1e12, 2),
+                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(c.flops_per_call / t_attn / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "prep_us": round(prep_ms / n * 1e3, 1), "merge_us": round(merge_ms / n * 1e3, 1)}
+
+
 def ulysses_leg(w, groups=4, reps=20):
     """One device's share of Ulysses degree 4 at the window's shape: pack its
     token shard of Q for the all-to-all, attention of its head group on the
@@ -361,6 +402,9 @@ def main():
         return 0
     if args.ulysses_only:
         print(json.dumps({"workload": w.name, "ulysses": ulysses_leg(w)}), flush=True)
+        return 0
+    if args.clip_only:
+        print(json.dumps({"workload": w.name, "clip77": clip_leg()}), flush=True)
         return 0
     if args.ring_split_only:
         qkv = synth.make_qkv(w, 0, 0, device="cuda")
@@ -462,6 +506,9 @@ def main():
         line["block"] = block_leg(w)
     drv.close()
     del drv
+    torch.cuda.empty_cache()
+    if not args.no_clip:
+        line["clip77"] = clip_leg()
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 oracle sample on the host", file=sys.stderr, flush=True)

@@ -650,32 +650,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 3: merge of split leftover tiles. Grid (rem tiles, BM): one block of
-// 4 waves per query row, D/64 head dims per lane. A tile held whole by one
-// workgroup returns at once. For row r over the segments s holding it:
+// Kernel 3: merge of split leftover tiles. Grid (rem tiles, BM MW / 4),
+// 256 threads: MW waves (1 or 4) per query row, D/64 head dims per lane. A
+// tile held whole by one workgroup returns at once. For row r over the
+// segments s holding it:
 //   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 //   lse = ln 2 (M + log2 sum_s 2^(m_s - M) l_s).
-// Wave w folds segments w, w + 4, ... in one pass with a running maximum; the
-// four partial results are then folded the same way.
+// Wave w of a row folds segments w, w + MW, ... in one pass with a running
+// maximum; with MW = 4 the four partial results are then folded the same
+// way (tiles split many ways), with MW = 1 a wave takes the whole row (few).
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, int MW>
 __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, float* __restrict__ lse,
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml, int N,
                                                     Sched sc, long long oh, long long on_stride) {
     constexpr int BM = NW * 32;
     constexpr int DPL = D / 64;  // head dims per lane (2 or 1)
-    constexpr int MW = 4;        // waves per row
+    static_assert(MW == 1 || MW == 4, "waves per row");
     const long long t = (long long)sc.full * sc.P + blockIdx.x;
     const long long y0 = (long long)blockIdx.x * sc.nkv;  // leftover unit offsets of tile t
     const int p0 = rem_owner(sc, y0);
     const int p1 = rem_owner(sc, y0 + sc.nkv - 1);
     if (p0 == p1) return;  // uniform over the block
     const int hd = (int)(t / sc.n_qtiles), qt = (int)(t % sc.n_qtiles);
-    const int r = blockIdx.y;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = blockIdx.y * (4 / MW) + wv / MW, w = wv % MW;
     const int qrow = qt * BM + r;
-    if (qrow >= N) return;  // uniform over the block
+    if (qrow >= N) return;  // uniform over the block when MW == 4
 
     // Partial slots: every workgroup after p0 starts its range inside tile
     // t, so t is its first leftover tile (slot 2p); p0's range starts in t
@@ -704,28 +706,33 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
         for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * a + b * x[i];
         M = Mn;
     }
-    __shared__ float sm_ml[MW][2];
-    __shared__ float sm_o[MW][D];
-    if (lane == 0) {
-        sm_ml[w][0] = M;
-        sm_ml[w][1] = L;
-    }
+    float Mt = M, Lt = L, at[DPL];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) sm_o[w][lane * DPL + i] = acc[i];
-    __syncthreads();
-    if (w != 0) return;
-    float Mt = sm_ml[0][0];
+    for (int i = 0; i < DPL; ++i) at[i] = acc[i];
+    if constexpr (MW > 1) {
+        __shared__ float sm_ml[MW][2];
+        __shared__ float sm_o[MW][D];
+        if (lane == 0) {
+            sm_ml[w][0] = M;
+            sm_ml[w][1] = L;
+        }
 #pragma unroll
-    for (int v = 1; v < MW; ++v) Mt = fmaxf(Mt, sm_ml[v][0]);
-    float Lt = 0.0f, at[DPL];
+        for (int i = 0; i < DPL; ++i) sm_o[w][lane * DPL + i] = acc[i];
+        __syncthreads();
+        if (w != 0) return;
+        Mt = sm_ml[0][0];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) at[i] = 0.0f;
+        for (int v = 1; v < MW; ++v) Mt = fmaxf(Mt, sm_ml[v][0]);
+        Lt = 0.0f;
 #pragma unroll
-    for (int v = 0; v < MW; ++v) {
-        const float b = __builtin_amdgcn_exp2f(sm_ml[v][0] - Mt);  // 0 for a wave with no segment
-        Lt += b * sm_ml[v][1];
+        for (int i = 0; i < DPL; ++i) at[i] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) at[i] += b * sm_o[v][lane * DPL + i];
+        for (int v = 0; v < MW; ++v) {
+            const float b = __builtin_amdgcn_exp2f(sm_ml[v][0] - Mt);  // 0 for a wave with no segment
+            Lt += b * sm_ml[v][1];
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) at[i] += b * sm_o[v][lane * DPL + i];
+        }
     }
     const float inv = 1.0f / Lt;
     if (lse != nullptr && lane == 0) lse[(size_t)hd * N + qrow] = (Mt + log2f(Lt)) * 0.69314718055994531f;

@@ -364,7 +364,9 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
     const int64_t rem_tiles = tiles - int64_t(sc.full) * h->P;
     sc.rem_units = rem_tiles * sc.nkv;
     sc.Prem = int(sc.rem_units < h->P ? (sc.rem_units > 0 ? sc.rem_units : 1) : h->P);
-    const dim3 mgrid{unsigned(rem_tiles), unsigned(kBM), 1u};
+    // Tiles split many ways merge with 4 waves per row, others with one.
+    const bool mw4 = sc.Prem >= 8 * rem_tiles;
+    const dim3 mgrid{unsigned(rem_tiles), unsigned(mw4 ? kBM : kBM / 4), 1u};
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
     const uint16_t* k16 = static_cast<const uint16_t*>(k);
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
@@ -403,9 +405,14 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
                            st, q16, h->d_kr, h->d_vt, o16, lse, tab, h->geo, Nq, Nk, Npad,
                            q_off, qh, qn, oh, on, sc, c2, int(!cross), h->d_part_o, h->d_part_ml);
         mark(2);
-        if (rem_tiles > 0)
-            hipLaunchKernelGGL((regen::merge_kernel<128, kNW>), mgrid, dim3(256), 0, st, o16, lse,
-                               h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
+        if (rem_tiles > 0) {
+            if (mw4)
+                hipLaunchKernelGGL((regen::merge_kernel<128, kNW, 4>), mgrid, dim3(256), 0, st, o16,
+                                   lse, h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
+            else
+                hipLaunchKernelGGL((regen::merge_kernel<128, kNW, 1>), mgrid, dim3(256), 0, st, o16,
+                                   lse, h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
+        }
     } else {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
                            h->d_vt, tab, h->geo, Nk, Npad, k_off, kh, kn);
@@ -414,9 +421,14 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
                            st, q16, h->d_kr, h->d_vt, o16, lse, tab, h->geo, Nq, Nk, Npad,
                            q_off, qh, qn, oh, on, sc, c2, int(!cross), h->d_part_o, h->d_part_ml);
         mark(2);
-        if (rem_tiles > 0)
-            hipLaunchKernelGGL((regen::merge_kernel<64, kNW>), mgrid, dim3(256), 0, st, o16, lse,
-                               h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
+        if (rem_tiles > 0) {
+            if (mw4)
+                hipLaunchKernelGGL((regen::merge_kernel<64, kNW, 4>), mgrid, dim3(256), 0, st, o16,
+                                   lse, h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
+            else
+                hipLaunchKernelGGL((regen::merge_kernel<64, kNW, 1>), mgrid, dim3(256), 0, st, o16,
+                                   lse, h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
+        }
     }
     hipError_t e = hipGetLastError();
     if (prof) {
