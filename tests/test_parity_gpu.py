@@ -125,6 +125,21 @@ def test_full_size_sampled_rows(name, step, block, rows):
     assert (of >= vf.amin(dim=1, keepdim=True) - 1e-2).all()
 
 
+def test_window_last_tiles_all_rows():
+    # The 25-frame window has 12 x 43 = 516 query tiles of 256 rows; on 256
+    # resident workgroups the last four (head 11, rows 9984..10919) are split
+    # over many workgroups and finished by the merge. Every row of them.
+    w = synth.WORKLOADS["window25_12x128_n10920"]
+    say("case window, every row of the last four query tiles")
+    q, k, v = synth.make_qkv(w, 1, 7, device="cuda")
+    o = run_gpu(q, k, v, w.grid)
+    rows = list(range(39 * 256, w.tokens))
+    ref = oracle.rope_attention(f64(q), f64(k), f64(v), w.grid, rows=rows)
+    got = f64(o)[:, rows, :]
+    check(got[-1], ref[-1], label="head 11, split tiles")
+    check(got, ref, label="all heads, rows of the last four tiles")
+
+
 # --------------------------------------------------------------------------
 # Edge cases: lengths around tile sizes, one token, one head, flags
 # --------------------------------------------------------------------------
