@@ -188,7 +188,7 @@ def block_leg(w, reps=10):
     """One self-attention block with random-init weights: QKV projection,
     3D-RoPE attention, output projection, timed as one unit, at the 1560-token
     block workload (12 x 128); the projection GEMM alone is also timed at the
-    window's size."""
+    window's size, and so is the output projection."""
     import torch
 
     from diffusion_transformer_attention_dit_amd import native, synth
@@ -225,6 +225,18 @@ def block_leg(w, reps=10):
     torch.cuda.synchronize()
     tg = a.elapsed_time(b) / reps * 1e-3
     gf = 2.0 * window.tokens * hid * 3 * hid
+    # The output projection alone at the window's token count.
+    wo = (torch.randn(hid, hid, generator=g, device="cuda") * hid ** -0.5).to(torch.bfloat16)
+    yo = torch.empty(window.tokens, hid, dtype=torch.bfloat16, device="cuda")
+    native.linear(xw, wo, out=yo, stream=stream)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        native.linear(xw, wo, out=yo, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    to = a.elapsed_time(b) / reps * 1e-3
+    go = 2.0 * window.tokens * hid * hid
     return {"what": "x[%d, %d] -> [Q|K|V] = x W_qkv^T -> attention -> y = O W_o^T (bf16, "
                     "random-init weights)" % (w.tokens, hid),
             "workload": w.name, "ms_per_block": round(t * 1e3, 4), "gflop": round(total / 1e9, 1),
@@ -233,7 +245,11 @@ def block_leg(w, reps=10):
             "qkv_projection_window": {"kernel": "gemm_nt_kernel", "shape": [window.tokens, hid, 3 * hid],
                                       "avg_launch_us": round(tg * 1e6, 2), "bound": "mfma",
                                       "achieved": round(gf / tg / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
-                                      "unit": "TFLOP/s", "frac": round(gf / tg / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+                                      "unit": "TFLOP/s", "frac": round(gf / tg / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "o_projection_window": {"kernel": "gemm_nt_kernel", "shape": [window.tokens, hid, hid],
+                                    "avg_launch_us": round(to * 1e6, 2), "bound": "mfma",
+                                    "achieved": round(go / to / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(go / to / 1e12 / PEAK_BF16_TFLOPS, 4)}}
 
 
 def cross_leg(w, reps=20):

@@ -4,12 +4,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <new>
 #include <string>
+#include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
@@ -670,11 +672,50 @@ void block_free(regen_block* b) {
     delete b;
 }
 
-void gemm(const uint16_t* A, int lda, const uint16_t* B, int ldb, uint16_t* C, int ldc, int M, int N,
-          int K, hipStream_t st) {
-    const dim3 grid{unsigned((M + regen::kGemmTile - 1) / regen::kGemmTile),
-                    unsigned((N + regen::kGemmTile - 1) / regen::kGemmTile), 1u};
-    hipLaunchKernelGGL(regen::gemm_nt_kernel, grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc, M, N, K);
+// Resident gemm_nt_kernel workgroups per device (CUs x workgroups per CU),
+// queried once per device.
+std::mutex g_gemm_mu;
+std::unordered_map<int, int> g_gemm_slots;
+
+regen_status gemm_slots(int* slots) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_gemm_mu);
+    auto it = g_gemm_slots.find(dev);
+    if (it != g_gemm_slots.end()) {
+        *slots = it->second;
+        return REGEN_OK;
+    }
+    int cus = 0, per_cu = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return fail_hip(e, "hipDeviceGetAttribute");
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, regen::gemm_nt_kernel, 256, 0)) !=
+        hipSuccess)
+        return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    *slots = std::max(1, cus) * std::max(1, per_cu);
+    g_gemm_slots[dev] = *slots;
+    return REGEN_OK;
+}
+
+regen_status gemm(const uint16_t* A, int lda, const uint16_t* B, int ldb, uint16_t* C, int ldc, int M,
+                  int N, int K, hipStream_t st) {
+    int slots = 1;
+    const regen_status s = gemm_slots(&slots);
+    if (s != REGEN_OK) return s;
+    const int64_t tiles = int64_t((M + regen::kGemmTile - 1) / regen::kGemmTile) *
+                          ((N + regen::kGemmTile - 1) / regen::kGemmTile);
+    // Quarter tiles for a short last round: only after at least one full
+    // round, and only if the quarters still fit in one round.
+    const int64_t full = tiles / slots * slots, rem = tiles - full;
+    const int64_t nfull = (full > 0 && rem > 0 && rem * 4 <= slots) ? full : tiles;
+    const int64_t blocks = nfull + (tiles - nfull) * 4;
+    if (blocks > INT32_MAX) return fail(REGEN_ERR_INVALID_ARGUMENT, "too many output tiles");
+    hipLaunchKernelGGL(regen::gemm_nt_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, A, lda, B, ldb,
+                       C, ldc, M, N, K, int(nfull));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip(e, "gemm_nt_kernel launch");
+    return REGEN_OK;
 }
 
 }  // namespace
@@ -706,12 +747,9 @@ regen_status regen_linear(const void* x, const void* w, void* y, int64_t rows, i
         (void)hipGetLastError();
         return fail(REGEN_ERR_NO_DEVICE, "no HIP device is available");
     }
-    gemm(static_cast<const uint16_t*>(x), in_features, static_cast<const uint16_t*>(w), in_features,
-         static_cast<uint16_t*>(y), out_features, int(rows), out_features, in_features,
-         static_cast<hipStream_t>(stream));
-    e = hipGetLastError();
-    if (e != hipSuccess) return fail_hip(e, "kernel launch");
-    return REGEN_OK;
+    return gemm(static_cast<const uint16_t*>(x), in_features, static_cast<const uint16_t*>(w),
+                in_features, static_cast<uint16_t*>(y), out_features, int(rows), out_features,
+                in_features, static_cast<hipStream_t>(stream));
 }
 
 regen_status regen_block_create(const regen_attn_desc* desc, regen_block_t* out) {
@@ -772,18 +810,16 @@ regen_status regen_block_forward(regen_block_t b, const void* x, const void* w_q
         return fail(REGEN_ERR_INVALID_ARGUMENT, "the current HIP device is not the block's device");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int Hd = b->hidden;
-    gemm(static_cast<const uint16_t*>(x), Hd, static_cast<const uint16_t*>(w_qkv), Hd, b->qkv, 3 * Hd,
-         b->N, 3 * Hd, Hd, st);
+    regen_status s = gemm(static_cast<const uint16_t*>(x), Hd, static_cast<const uint16_t*>(w_qkv), Hd,
+                          b->qkv, 3 * Hd, b->N, 3 * Hd, Hd, st);
+    if (s != REGEN_OK) return s;
     const long long D = b->attn->p.head_dim;
     const Strides sd{D, 3LL * Hd, D, 3LL * Hd, D, Hd};
-    regen_status s = enqueue(b->attn, b->qkv, 0, b->N, b->qkv + Hd, b->qkv + 2 * Hd, 0, b->N,
+    s = enqueue(b->attn, b->qkv, 0, b->N, b->qkv + Hd, b->qkv + 2 * Hd, 0, b->N,
                              b->attn_out, nullptr, stream, false, sd);
     if (s != REGEN_OK) return s;
-    gemm(b->attn_out, Hd, static_cast<const uint16_t*>(w_o), Hd, static_cast<uint16_t*>(y), Hd, b->N,
-         Hd, Hd, st);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail_hip(e, "kernel launch");
-    return REGEN_OK;
+    return gemm(b->attn_out, Hd, static_cast<const uint16_t*>(w_o), Hd, static_cast<uint16_t*>(y), Hd,
+                b->N, Hd, Hd, st);
 }
 
 regen_status regen_block_destroy(regen_block_t b) {

@@ -53,6 +53,9 @@ def test_block_all_elements(name):
 @pytest.mark.parametrize("rows,fin,fout", [
     (1, 64, 1), (37, 64, 100), (128, 128, 128), (1000, 256, 129), (300, 1536, 4608),
     (1560, 1536, 4608), (10920, 1536, 1536),
+    # 33 x 16 = 528 tiles of 128 x 128: one full round on 256 CUs x 2, the
+    # last 16 tiles (ragged rows and columns among them) as 64 x 64 quarters
+    (4100, 256, 2000),
 ])
 def test_linear_against_fp64(rows, fin, fout):
     say("case linear rows=%d in=%d out=%d" % (rows, fin, fout))
