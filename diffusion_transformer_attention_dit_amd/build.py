@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libregen_attn.so")
 SOURCES = [os.path.join(CSRC, "regen_attn.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, "kernels.hpp"), os.path.join(INCLUDE, "regen_attn.h")]
+DEPENDS = SOURCES + [os.path.join(CSRC, h) for h in ("common.hpp", "attention.hpp", "gemm.hpp", "layout.hpp")] + \
+    [os.path.join(INCLUDE, "regen_attn.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1,6 +1,5 @@
-// Device kernels of regen_attn for CDNA4 (gfx950).
-//
-// Two kernels make one attention call:
+// The attention kernels of regen_attn for CDNA4 (gfx950). One attention
+// call runs the first two, and the third when the schedule split tiles:
 //
 //  1. rope_k_vt_kernel (HBM-bound pass over K and V): applies the 3D rotary
 //     embedding to K and rounds it to bf16 into Kr, and writes V transposed
@@ -15,6 +14,8 @@
 //     softmax (running max, running sum) in registers.
 //  3. merge_kernel: finishes query tiles whose key blocks were split over
 //     several workgroups.
+// merge_parts_kernel combines results over disjoint key sets (the Ring
+// step).
 //
 // The attention is the one ReGenVC's decoder transformer evaluates over the
 // window's latent tokens (arXiv 2607.28144, blog summary "Methodology - deep
@@ -23,29 +24,19 @@
 // (index page, "Builds on") but is laid out here for 64-lane wavefronts and
 // 32x32x16 bf16 MFMA.
 //
-// MFMA v_mfma_f32_32x32x16_bf16 operand layout (lane l, c = l % 32,
-// g = l / 32): A supplies row c, k = 8g..8g+7; B supplies column c,
-// k = 8g..8g+7; the 16 fp32 results of lane l are D[row = 8(i/4) + 4g + i%4]
-// [column c], i = 0..15.
-//
 // Attention is computed transposed, S^T = K Q^T, so that a lane's results
-// all belong to ONE query (its column c) and 16 keys: the row max and row
+// all belong to ONE query (its column c in the MFMA layout of common.hpp)
+// and 16 keys: the row max and row
 // sum are in-lane reductions plus one exchange with lane l ^ 32
 // (v_permlane32_swap), and the O^T = V^T P^T product consumes the
 // probabilities straight from registers as its B operand. The key order that
 // the B operand then implies (slot 8g + j <-> key 8(j/4) + 4g + j%4 inside
-// each group of 16) is baked into Vt by the first kernel.
+// each group of 16) is baked into Vt by rope_k_vt_kernel.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "common.hpp"
 
 namespace regen {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPrepKeys = 128;  // workspace padding unit (keys)
 constexpr int kPrepBlock = 64;  // keys per rope_k_vt block: one Kr / Vt tile
@@ -58,15 +49,6 @@ struct RopeGeom {
     int pairs[3];
     int off[3];
 };
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Round two floats to bf16 (round-to-nearest-even, v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    f32x2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 // (cos, sin) for rotary pair i of a token at (t, h, w).
 __device__ __forceinline__ float2 rope_cs(const float2* __restrict__ tab, const RopeGeom& g,
@@ -101,7 +83,7 @@ __device__ __forceinline__ uint4 rope_chunk(uint4 in, const float2* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: K rotation + V transpose. Grid (Npad / 64, heads), 256 threads.
+// rope_k_vt_kernel: K rotation + V transpose. Grid (Npad / 64, heads), 256 threads.
 //   k, v : bf16, key n of head h at element h * sh + n * sn (head-major
 //          [heads][N][D]: sh = N D, sn = D; token-major [N][heads][D]:
 //          sh = D, sn = heads D), key n being token n_off + n of the grid.
@@ -194,44 +176,6 @@ __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     }
 }
 
-// Logical block id with consecutive ids on one XCD. Blocks are dispatched
-// round-robin over the 8 XCDs (block b runs on XCD b % 8); this maps each
-// XCD's blocks onto one contiguous range of logical ids, so that the blocks
-// sharing an XCD's L2 work on the same head's K/V.
-__device__ __forceinline__ int xcd_remap(int b, int G) {
-    const int per = G / 8, rem = G % 8, x = b % 8, loc = b / 8;
-    return (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
-}
-
-// Byte offset of 16-byte chunk c of row r in an LDS tile whose rows are RB
-// bytes (128 or 256) and stored unpadded. Chunks are XOR-swizzled by row so
-// that the MFMA operand reads (32 rows, one chunk column) are free of bank
-// conflicts; the swizzle is its own inverse.
-template <int RB>
-__device__ __forceinline__ int swz_off(int r, int c) {
-    static_assert(RB == 128 || RB == 256, "row bytes");
-    const int pc = (RB == 256) ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
-    return r * RB + pc * 16;
-}
-
-// Buffer resource over `bytes` bytes at `base` (raw, untyped 32-bit data
-// format); accesses past `bytes` read as zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-// One wave-wide 16-byte-per-lane copy global -> LDS without registers
-// (buffer_load_dwordx4 ... lds): lane i's 16 bytes, read at byte `voff` of
-// the resource, land at lds_wave_base + 16 i. The MUBUF form is used rather
-// than the global (FLAT) one so that LDS reads issued while copies are in
-// flight keep precise, in-order wait counts.
-__device__ __forceinline__ void g2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
-                                        void* lds_wave_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_wave_base,
-                                             16, voff, 0, 0, 0);
-}
-
 // Issue the copies of K tile j and Vt tile j into LDS buffer (ks, vs). Both
 // are stored in HBM as runs of 1 KiB MFMA operand fragments in lane order,
 // which land unchanged in LDS: run r of a tile goes to byte 1024 r of the
@@ -316,11 +260,11 @@ __device__ __forceinline__ bool get_segment(const Sched& sc, int p, int k, long 
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: attention, persistent. Grid P, NW * 64 threads.
+// attn_fwd_kernel: attention, persistent. Grid P, NW * 64 threads.
 //   q, o    : bf16, row m of head h at element h * qh + m * qn of q and
 //             h * oh + m * on of o (head-major, token-major or a strided
 //             token-major view), row m being token q_off + m
-//   Kr, Vt  : the Nk keys prepared by kernel 1 (Npad rows per head)
+//   Kr, Vt  : the Nk keys prepared by rope_k_vt_kernel (Npad rows per head)
 //   lse     : [heads][Nq] fp32 log-sum-exp of each row's scores, or null
 //   part_o  : [2P][BM][D] fp32 unnormalised O of split tiles
 //   part_ml : [2P][BM][2] fp32 (m, l) of split tiles
@@ -650,7 +594,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 3: merge of split leftover tiles. Grid (rem tiles, BM MW / 4),
+// merge_kernel: merge of split leftover tiles. Grid (rem tiles, BM MW / 4),
 // 256 threads: MW waves (1 or 4) per query row, D/64 head dims per lane. A
 // tile held whole by one workgroup returns at once. For row r over the
 // segments s holding it:
@@ -746,7 +690,7 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 4: combine attention results over disjoint key sets (Ring-style key
+// merge_parts_kernel: combine attention results over disjoint key sets (Ring-style key
 // splitting keeps attention exact this way). Part i holds O_i [rows][D] bf16,
 // normalised over its own keys, and lse_i [rows] fp32; over the union of the
 // key sets
@@ -804,162 +748,6 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(MergeParts parts, int 
         make_uint4(pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv),
                    pack_bf16(acc[4] * inv, acc[5] * inv), pack_bf16(acc[6] * inv, acc[7] * inv));
     if (lse != nullptr && c == 0) lse[row] = m + logf(z);
-}
-
-// ---------------------------------------------------------------------------
-// Kernel 5: the on-device half of a Ulysses all-to-all (blog summary,
-// "Methodology - deep read", USP paragraph: Ulysses turns sequence shards
-// into head shards). A block transpose src [A][B][E] -> dst [B][A][E] of
-// E-byte blocks, 16 bytes per thread, writes in destination order:
-//   pack   [Nl][G][H/G][D] -> [G][Nl][H/G][D]  (A = Nl, B = G)
-//   unpack [G][Nl][H/G][D] -> [Nl][G][H/G][D]  (A = G, B = Nl)
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void block_transpose_kernel(const uint4* __restrict__ src,
-                                                              uint4* __restrict__ dst, long long A,
-                                                              long long B, long long E16) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= A * B * E16) return;
-    const long long e = i % E16, ba = i / E16;
-    const long long a = ba % A, b = ba / A;
-    dst[i] = src[(a * B + b) * E16 + e];
-}
-
-// ---------------------------------------------------------------------------
-// Kernel 6: a linear layer without bias, C = A B^T: A [M][K] (row stride
-// lda), B [N][K] (row stride ldb: the [out][in] weight of the layer), C [M][N]
-// (row stride ldc); bf16 in, fp32 accumulation, bf16 out (RNE). K % 64 == 0.
-// A workgroup of 4 waves computes a 128 x 128 tile (64 x 64 per wave, 2 x 2
-// MFMA blocks) or a 64 x 64 quarter tile (32 x 32 per wave), with K steps of
-// 64 through double-buffered LDS filled by LDS-DMA copies (128-byte rows,
-// chunk ^ ((row >> 1) & 7)). Rows past M or N read as zero (buffer
-// resources) and are not stored.
-// ---------------------------------------------------------------------------
-constexpr int kGemmTile = 128, kGemmBK = 64;
-constexpr int kGemmTileBytes = kGemmTile * kGemmBK * 2;
-
-// Copies of the first 32 RUNS rows x 64 k of a tile (RUNS runs of 1 KiB per
-// wave; RUNS = 4: all 128 rows, RUNS = 2: 64 rows).
-template <int RUNS>
-__device__ __forceinline__ void gemm_issue(__amdgpu_buffer_rsrc_t rs, int ld, int row0, int k0,
-                                           char* lds, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < RUNS; ++i) {
-        const int run = i * 4 + wave;
-        const int p = run * 64 + lane;  // chunk position in the tile
-        const int r = p >> 3, pc = p & 7;
-        const int c = pc ^ ((r >> 1) & 7);  // the logical chunk stored at pc
-        g2lds16(rs, (uint32_t)(((long long)(row0 + r) * ld + k0 + c * 8) * 2), lds + run * 1024);
-    }
-}
-
-// One (2 WT) x (2 WT) output tile at (m0, n0), WT x WT per wave (WT = 64 or
-// 32). The MFMA computes the tile transposed (B rows as its first operand), so
-// that a lane ends up with 4 consecutive columns of one output row: 8-byte
-// stores.
-template <int WT>
-__device__ __forceinline__ void gemm_tile(__amdgpu_buffer_rsrc_t ra, int lda,
-                                          __amdgpu_buffer_rsrc_t rb, int ldb,
-                                          uint16_t* __restrict__ C, int ldc, int M, int N, int K,
-                                          int m0, int n0, char (*smem)[2][kGemmTileBytes]) {
-    constexpr int NB = WT / 32, RUNS = WT / 16;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = lane & 31, half = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
-    f32x16 acc[NB][NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    gemm_issue<RUNS>(ra, lda, m0, 0, smem[0][0], wave, lane);
-    gemm_issue<RUNS>(rb, ldb, n0, 0, smem[0][1], wave, lane);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int nk = K / kGemmBK;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) {
-            gemm_issue<RUNS>(ra, lda, m0, (kt + 1) * kGemmBK, smem[buf ^ 1][0], wave, lane);
-            gemm_issue<RUNS>(rb, ldb, n0, (kt + 1) * kGemmBK, smem[buf ^ 1][1], wave, lane);
-        }
-        const char* as = smem[buf][0];
-        const char* bs = smem[buf][1];
-#pragma unroll
-        for (int kk = 0; kk < kGemmBK / 16; ++kk) {
-            bf16x8 a[NB], b[NB];
-#pragma unroll
-            for (int i = 0; i < NB; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(as + swz_off<128>(wm * WT + i * 32 + col, kk * 2 + half));
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-                b[j] = *reinterpret_cast<const bf16x8*>(bs + swz_off<128>(wn * WT + j * 32 + col, kk * 2 + half));
-#pragma unroll
-            for (int i = 0; i < NB; ++i)
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-        }
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
-    // Lane (col, half) holds C[m][n] for m = its row col of the block and
-    // n = 8 g + 4 half + e (g, e < 4) of the block's 32 columns.
-    const bool st8 = (ldc & 3) == 0;  // 8-byte aligned runs of 4
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int m = m0 + wm * WT + i * 32 + col;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WT + j * 32 + g * 8 + half * 4;
-                const f32x16& v = acc[i][j];
-                uint16_t* cp = C + (long long)m * ldc + n;
-                if (st8 && n + 3 < N) {
-                    *reinterpret_cast<uint2*>(cp) = make_uint2(pack_bf16(v[g * 4], v[g * 4 + 1]),
-                                                               pack_bf16(v[g * 4 + 2], v[g * 4 + 3]));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) cp[e] = (uint16_t)(pack_bf16(v[g * 4 + e], 0.0f) & 0xffffu);
-                }
-            }
-    }
-}
-
-// The 128 x 128 tiles are numbered in groups of 8 tile rows (column-major
-// inside a group), so that workgroups running together share A and B tiles
-// in L2. Workgroups [0, nfull) take tiles [0, nfull), remapped so that each
-// XCD walks one contiguous range of them. When the tile count leaves a last
-// round that would keep only a few CUs busy, the host makes nfull the tiles
-// of the full rounds, and workgroups nfull.. take each remaining tile as four
-// 64 x 64 quarters, spreading that round over four times as many CUs.
-__global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict__ A, int lda,
-                                                      const uint16_t* __restrict__ B, int ldb,
-                                                      uint16_t* __restrict__ C, int ldc, int M,
-                                                      int N, int K, int nfull) {
-    __shared__ __attribute__((aligned(1024))) char smem[2][2][kGemmTileBytes];  // [buffer][A, B]
-    constexpr int GM = 8;
-    const int mt = (M + kGemmTile - 1) / kGemmTile, nt = (N + kGemmTile - 1) / kGemmTile;
-    const int bid = blockIdx.x;
-    const int t = bid < nfull ? xcd_remap(bid, nfull) : nfull + (bid - nfull) / 4;
-    const int first = (t / (GM * nt)) * GM;
-    const int gm = min(mt - first, GM);
-    const int r = t - first * nt;
-    int m0 = (first + r % gm) * kGemmTile, n0 = (r / gm) * kGemmTile;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)((long long)M * lda * 2));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)((long long)N * ldb * 2));
-    if (bid < nfull) {
-        gemm_tile<64>(ra, lda, rb, ldb, C, ldc, M, N, K, m0, n0, smem);
-    } else {
-        const int quarter = (bid - nfull) & 3;
-        m0 += (quarter >> 1) * 64;
-        n0 += (quarter & 1) * 64;
-        gemm_tile<32>(ra, lda, rb, ldb, C, ldc, M, N, K, m0, n0, smem);
-    }
 }
 
 }  // namespace regen

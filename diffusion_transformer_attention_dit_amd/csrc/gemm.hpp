@@ -1,0 +1,146 @@
+// The projection GEMM of the self-attention block (CDNA4, gfx950).
+#pragma once
+
+#include "common.hpp"
+
+namespace regen {
+
+// ---------------------------------------------------------------------------
+// gemm_nt_kernel: a linear layer without bias, C = A B^T: A [M][K] (row stride
+// lda), B [N][K] (row stride ldb: the [out][in] weight of the layer), C [M][N]
+// (row stride ldc); bf16 in, fp32 accumulation, bf16 out (RNE). K % 64 == 0.
+// A workgroup of 4 waves computes a 128 x 128 tile (64 x 64 per wave, 2 x 2
+// MFMA blocks) or a 64 x 64 quarter tile (32 x 32 per wave), with K steps of
+// 64 through double-buffered LDS filled by LDS-DMA copies (128-byte rows,
+// chunk ^ ((row >> 1) & 7)). Rows past M or N read as zero (buffer
+// resources) and are not stored.
+// ---------------------------------------------------------------------------
+constexpr int kGemmTile = 128, kGemmBK = 64;
+constexpr int kGemmTileBytes = kGemmTile * kGemmBK * 2;
+
+// Copies of the first 32 RUNS rows x 64 k of a tile (RUNS runs of 1 KiB per
+// wave; RUNS = 4: all 128 rows, RUNS = 2: 64 rows).
+template <int RUNS>
+__device__ __forceinline__ void gemm_issue(__amdgpu_buffer_rsrc_t rs, int ld, int row0, int k0,
+                                           char* lds, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < RUNS; ++i) {
+        const int run = i * 4 + wave;
+        const int p = run * 64 + lane;  // chunk position in the tile
+        const int r = p >> 3, pc = p & 7;
+        const int c = pc ^ ((r >> 1) & 7);  // the logical chunk stored at pc
+        g2lds16(rs, (uint32_t)(((long long)(row0 + r) * ld + k0 + c * 8) * 2), lds + run * 1024);
+    }
+}
+
+// One (2 WT) x (2 WT) output tile at (m0, n0), WT x WT per wave (WT = 64 or
+// 32). The MFMA computes the tile transposed (B rows as its first operand), so
+// that a lane ends up with 4 consecutive columns of one output row: 8-byte
+// stores.
+template <int WT>
+__device__ __forceinline__ void gemm_tile(__amdgpu_buffer_rsrc_t ra, int lda,
+                                          __amdgpu_buffer_rsrc_t rb, int ldb,
+                                          uint16_t* __restrict__ C, int ldc, int M, int N, int K,
+                                          int m0, int n0, char (*smem)[2][kGemmTileBytes]) {
+    constexpr int NB = WT / 32, RUNS = WT / 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1;
+    f32x16 acc[NB][NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    gemm_issue<RUNS>(ra, lda, m0, 0, smem[0][0], wave, lane);
+    gemm_issue<RUNS>(rb, ldb, n0, 0, smem[0][1], wave, lane);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int nk = K / kGemmBK;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) {
+            gemm_issue<RUNS>(ra, lda, m0, (kt + 1) * kGemmBK, smem[buf ^ 1][0], wave, lane);
+            gemm_issue<RUNS>(rb, ldb, n0, (kt + 1) * kGemmBK, smem[buf ^ 1][1], wave, lane);
+        }
+        const char* as = smem[buf][0];
+        const char* bs = smem[buf][1];
+#pragma unroll
+        for (int kk = 0; kk < kGemmBK / 16; ++kk) {
+            bf16x8 a[NB], b[NB];
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(as + swz_off<128>(wm * WT + i * 32 + col, kk * 2 + half));
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(bs + swz_off<128>(wn * WT + j * 32 + col, kk * 2 + half));
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+        }
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    // Lane (col, half) holds C[m][n] for m = its row col of the block and
+    // n = 8 g + 4 half + e (g, e < 4) of the block's 32 columns.
+    const bool st8 = (ldc & 3) == 0;  // 8-byte aligned runs of 4
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int m = m0 + wm * WT + i * 32 + col;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WT + j * 32 + g * 8 + half * 4;
+                const f32x16& v = acc[i][j];
+                uint16_t* cp = C + (long long)m * ldc + n;
+                if (st8 && n + 3 < N) {
+                    *reinterpret_cast<uint2*>(cp) = make_uint2(pack_bf16(v[g * 4], v[g * 4 + 1]),
+                                                               pack_bf16(v[g * 4 + 2], v[g * 4 + 3]));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) cp[e] = (uint16_t)(pack_bf16(v[g * 4 + e], 0.0f) & 0xffffu);
+                }
+            }
+    }
+}
+
+// The 128 x 128 tiles are numbered in groups of 8 tile rows (column-major
+// inside a group), so that workgroups running together share A and B tiles
+// in L2. Workgroups [0, nfull) take tiles [0, nfull), remapped so that each
+// XCD walks one contiguous range of them. When the tile count leaves a last
+// round that would keep only a few CUs busy, the host makes nfull the tiles
+// of the full rounds, and workgroups nfull.. take each remaining tile as four
+// 64 x 64 quarters, spreading that round over four times as many CUs.
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict__ A, int lda,
+                                                      const uint16_t* __restrict__ B, int ldb,
+                                                      uint16_t* __restrict__ C, int ldc, int M,
+                                                      int N, int K, int nfull) {
+    __shared__ __attribute__((aligned(1024))) char smem[2][2][kGemmTileBytes];  // [buffer][A, B]
+    constexpr int GM = 8;
+    const int mt = (M + kGemmTile - 1) / kGemmTile, nt = (N + kGemmTile - 1) / kGemmTile;
+    const int bid = blockIdx.x;
+    const int t = bid < nfull ? xcd_remap(bid, nfull) : nfull + (bid - nfull) / 4;
+    const int first = (t / (GM * nt)) * GM;
+    const int gm = min(mt - first, GM);
+    const int r = t - first * nt;
+    int m0 = (first + r % gm) * kGemmTile, n0 = (r / gm) * kGemmTile;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)((long long)M * lda * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)((long long)N * ldb * 2));
+    if (bid < nfull) {
+        gemm_tile<64>(ra, lda, rb, ldb, C, ldc, M, N, K, m0, n0, smem);
+    } else {
+        const int quarter = (bid - nfull) & 3;
+        m0 += (quarter >> 1) * 64;
+        n0 += (quarter & 1) * 64;
+        gemm_tile<32>(ra, lda, rb, ldb, C, ldc, M, N, K, m0, n0, smem);
+    }
+}
+
+}  // namespace regen

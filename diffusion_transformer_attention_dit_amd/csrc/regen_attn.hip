@@ -15,7 +15,9 @@
 #include <unordered_set>
 #include <vector>
 
-#include "kernels.hpp"
+#include "attention.hpp"
+#include "gemm.hpp"
+#include "layout.hpp"
 
 namespace {
 
