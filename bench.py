@@ -258,7 +258,7 @@ def block_leg(w, reps=10):
 
 def cross_leg(w, reps=20):
     """Cross-attention of the window's tokens to conditioning tokens (77,
-    the assumed encoder context, and 512): time per call against the HBM
+    the assumed encoder context, 226 and 512): time per call against the HBM
     roofline (reading Q and writing O dominate; the context is small)."""
     import torch
 
@@ -269,7 +269,7 @@ def cross_leg(w, reps=20):
     attn = native.Attention(w.heads, w.head_dim, w.grid)
     out = {"what": "all %d tokens x %d heads attend to ctx_len conditioning tokens, no rotation"
                    % (w.tokens, w.heads)}
-    for ctx in (synth.CONTEXT_TOKENS, 512):
+    for ctx in (synth.CONTEXT_TOKENS, 226, 512):
         kc, vc = synth.make_context(w, ctx, device="cuda")
         attn.forward_cross(q, kc, vc, out=o, stream=stream)
         torch.cuda.synchronize()

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "attention.hpp"
+#include "cross.hpp"
 #include "gemm.hpp"
 #include "layout.hpp"
 
@@ -139,6 +140,7 @@ struct regen_attn {
     uint16_t* d_kr;  // workspace: rotated K
     uint16_t* d_vt;  // workspace: transposed V
     int P;           // persistent attention workgroups
+    int Pc;          // cross_attn_kernel workgroups (one round of resident slots)
     float* d_part_o;   // split-tile partial O   [2P][BM][D]
     float* d_part_ml;  // split-tile (m, l)       [2P][BM][2]
 };
@@ -146,11 +148,15 @@ struct regen_attn {
 namespace {
 
 template <int D>
-regen_status occupancy(int* blocks_per_cu) {
+regen_status occupancy(int* blocks_per_cu, int* cross_blocks_per_cu) {
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         blocks_per_cu, regen::attn_fwd_kernel<D, kBN, kNW>, kNW * 64, 0);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            cross_blocks_per_cu, regen::cross_attn_kernel<D, kNW, true>, kNW * 64, 0);
     if (e != hipSuccess) return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     if (*blocks_per_cu < 1) *blocks_per_cu = 1;
+    if (*cross_blocks_per_cu < 1) *cross_blocks_per_cu = 1;
     return REGEN_OK;
 }
 
@@ -236,14 +242,15 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
     h->d_tab = h->d_tab_id = nullptr;
     h->d_kr = h->d_vt = nullptr;
     h->d_part_o = h->d_part_ml = nullptr;
-    int per_cu = 1;
-    s = p.head_dim == 128 ? occupancy<128>(&per_cu) : occupancy<64>(&per_cu);
+    int per_cu = 1, cross_per_cu = 1;
+    s = p.head_dim == 128 ? occupancy<128>(&per_cu, &cross_per_cu) : occupancy<64>(&per_cu, &cross_per_cu);
     if (s != REGEN_OK) {
         delete h;
         return s;
     }
     const int64_t slots = int64_t(per_cu) * prop.multiProcessorCount;
     h->P = int(slots < p.units ? slots : p.units);
+    h->Pc = cross_per_cu * prop.multiProcessorCount;
 
     const size_t tab_bytes = tab.size() * sizeof(float2);
     const size_t half_ws = workspace_bytes(p) / 2;
@@ -401,7 +408,29 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
         if (prof) (void)hipEventRecord(rec.ev[i], st);
     };
 
-    if (p.head_dim == 128) {
+    // A short context stays in LDS: one kernel, one pass over the queries.
+    const bool short_ctx = cross && nk <= regen::kCrossMaxKeys && nk * kn * 2 < (int64_t(1) << 31);
+    const int64_t cross_units = int64_t(p.heads) * ((nq + 31) / 32);
+    const dim3 cgrid{unsigned(std::min<int64_t>(h->Pc, cross_units)), 1u, 1u};
+    if (short_ctx) {
+        mark(1);
+        if (p.head_dim == 128) {
+            if (lse)
+                hipLaunchKernelGGL((regen::cross_attn_kernel<128, kNW, true>), cgrid, dim3(kNW * 64), 0, st,
+                                   q16, k16, v16, o16, lse, Nq, Nk, qh, qn, kh, kn, oh, on, p.heads, c2);
+            else
+                hipLaunchKernelGGL((regen::cross_attn_kernel<128, kNW, false>), cgrid, dim3(kNW * 64), 0, st,
+                                   q16, k16, v16, o16, lse, Nq, Nk, qh, qn, kh, kn, oh, on, p.heads, c2);
+        } else {
+            if (lse)
+                hipLaunchKernelGGL((regen::cross_attn_kernel<64, kNW, true>), cgrid, dim3(kNW * 64), 0, st,
+                                   q16, k16, v16, o16, lse, Nq, Nk, qh, qn, kh, kn, oh, on, p.heads, c2);
+            else
+                hipLaunchKernelGGL((regen::cross_attn_kernel<64, kNW, false>), cgrid, dim3(kNW * 64), 0, st,
+                                   q16, k16, v16, o16, lse, Nq, Nk, qh, qn, kh, kn, oh, on, p.heads, c2);
+        }
+        mark(2);
+    } else if (p.head_dim == 128) {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<128>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
                            h->d_vt, tab, h->geo, Nk, Npad, k_off, kh, kn);
         mark(1);

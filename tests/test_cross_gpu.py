@@ -67,6 +67,25 @@ def test_cross_window_sampled(ctx_len):
     check_o(f64(o)[:, rows], ref, "cross window %d" % ctx_len)
 
 
+@pytest.mark.parametrize("ctx_len", [1, 77, 200, 300])
+def test_cross_head_dim_64(ctx_len):
+    # head_dim 64 (one head, 1560 tokens); contexts up to 256 keys run in the
+    # short-context kernel, longer ones in the persistent one.
+    w = synth.WORKLOADS["tiny_1x64_n128"]
+    grid = (4, 15, 26)
+    say("case cross-attention head_dim 64, ctx %d" % ctx_len)
+    q, _, _ = synth.make_qkv(w, device="cuda", grid=grid)
+    kc, vc = synth.make_context(w, ctx_len, device="cuda")
+    attn = native.Attention(w.heads, w.head_dim, grid)
+    o, lse = attn.forward_cross(q, kc, vc, lse=None)
+    torch.cuda.synchronize()
+    attn.close()
+    ref_o, ref_lse = oracle.c_attention(f64(q), f64(kc), f64(vc), return_lse=True)
+    check_o(f64(o), ref_o, "cross d64 %d" % ctx_len)
+    d = np.abs(lse.cpu().double().numpy() - ref_lse)
+    assert d.max() <= 2e-2 and d.mean() <= 2e-3, (d.max(), d.mean())
+
+
 def test_cross_token_major_matches_head_major():
     w = synth.WORKLOADS["block_12x128_n1560"]
     say("case cross-attention token-major")
