@@ -109,7 +109,9 @@ typedef struct regen_attn *regen_attn_t;
  * On success *out receives the handle; on any failure *out is set to NULL
  * (when out is not NULL) and the status says why:
  *   INVALID_ARGUMENT (NULL desc/out, wrong struct_size, heads/grid < 1,
- *   bad pairs split, base or scale < 0, unknown flags, tokens > 2^30),
+ *   bad pairs split, base or scale < 0, unknown flags, tokens > 2^30, one
+ *   head's rotated K reaching 2^31 bytes: ceil(tokens/128)*128 * head_dim *
+ *   2 >= 2^31),
  *   UNSUPPORTED (head_dim not 64/128, current device is not gfx950),
  *   NO_DEVICE, OUT_OF_MEMORY, HIP.
  */
@@ -169,7 +171,10 @@ regen_status regen_attn_forward_range(regen_attn_t h, const void *q, int64_t q_b
  *   o      : like q;  lse : [heads][tokens] fp32 or NULL
  * 1 <= ctx_len <= grid_t*grid_h*grid_w (the workspace is sized by the
  * window). Same pointer rules, ordering rule and errors as
- * regen_attn_forward_range.
+ * regen_attn_forward_range. A context of at most 256 tokens is held whole in
+ * on-chip memory by one kernel that reads k_ctx and v_ctx directly (the
+ * handle's workspace is not touched); longer ones go through the workspace
+ * like regen_attn_forward.
  */
 regen_status regen_attn_forward_cross(regen_attn_t h, const void *q, const void *k_ctx,
                                       const void *v_ctx, int64_t ctx_len, void *o, float *lse,
@@ -284,7 +289,8 @@ const char *regen_attn_last_error(void);
  * Kernel timing for handles created with REGEN_ATTN_PROFILE. Each forward
  * then records HIP events on its stream around each of its three kernels
  * (the K-rotation / V-transpose pass, the attention kernel, the merge of
- * tiles split across workgroups). This call waits for the events of every
+ * tiles split across workgroups; a short-context cross-attention call runs
+ * one kernel, counted as the attention kernel). This call waits for the events of every
  * forward issued since the last read, adds their durations (milliseconds)
  * to *prep_ms, *attn_ms, *merge_ms and the number of forwards to *calls
  * (each output may be NULL), and forgets them.
