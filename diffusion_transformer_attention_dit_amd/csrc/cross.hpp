@@ -26,8 +26,8 @@ constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 //             of head h at element h * kh + n * kn (not rotated)
 //   lse     : [heads][Nq] fp32 log-sum-exp of each row's scores, or null
 // A unit is 32 query rows of one head (one wave's share), units numbered
-// head-major, U of them. Workgroup p takes units [p U / G, (p + 1) U / G):
-// for each head in that range it copies the head's context to LDS in the
+// head-major. Each workgroup takes a contiguous range of units (below): for
+// each head in that range it copies the head's context to LDS in the
 // Kr / Vt fragment layout of rope_k_vt_kernel (K gathered by the copies
 // themselves, V copied row by row and transposed in LDS), then its waves
 // take the head's units in turn, each unit
@@ -51,9 +51,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31, half = lane >> 5;
     const int upH = (Nq + 31) / 32;  // units per head
-    const long long U = (long long)heads * upH;
-    const int pid = xcd_remap(blockIdx.x, gridDim.x);
-    const long long u_begin = U * pid / gridDim.x, u_end = U * (pid + 1) / gridDim.x;
+    // Workgroup p's units: with at least as many workgroups as heads, head h
+    // gets workgroups [h G / heads, (h + 1) G / heads) and each of them an
+    // equal share of the head's units, so that no workgroup builds two
+    // contexts; with fewer, workgroup p takes whole heads
+    // [p heads / G, (p + 1) heads / G). Consecutive workgroups share an XCD.
+    const int G = gridDim.x;
+    const int pid = xcd_remap(blockIdx.x, G);
+    long long u_begin, u_end;
+    if (G >= heads) {
+        int h = (int)(((long long)pid * heads) / G);
+        while (h + 1 < heads && ((long long)(h + 1) * G) / heads <= pid) ++h;
+        while (((long long)h * G) / heads > pid) --h;
+        const int b0 = (int)(((long long)h * G) / heads), n = (int)(((long long)(h + 1) * G) / heads) - b0;
+        u_begin = (long long)h * upH + (long long)upH * (pid - b0) / n;
+        u_end = (long long)h * upH + (long long)upH * (pid - b0 + 1) / n;
+    } else {
+        u_begin = (long long)upH * (((long long)pid * heads) / G);
+        u_end = (long long)upH * (((long long)(pid + 1) * heads) / G);
+    }
     const int nkv = (Nk + BN - 1) / BN;
     const uint32_t kv_bytes = (uint32_t)(((long long)(Nk - 1) * kn_stride + D) * 2);
     constexpr int NKF = KBYTES / 1024, NVF = VBYTES / 1024;  // 1 KiB fragments per K / Vt tile
