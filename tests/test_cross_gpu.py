@@ -36,7 +36,9 @@ def check_o(got, ref, label):
     assert ma <= MAX_ABS and mr <= MEAN_REL, (label, ma, mr)
 
 
-@pytest.mark.parametrize("ctx_len", [1, 64, 77, 226, 512, 1000])
+# 1..256 run in the short-context kernel (256: four full key tiles), 257 and
+# up in the persistent one.
+@pytest.mark.parametrize("ctx_len", [1, 64, 77, 226, 256, 257, 512, 1000])
 def test_cross_block_all_elements(ctx_len):
     w = synth.WORKLOADS["block_12x128_n1560"]
     say("case cross-attention block, ctx %d" % ctx_len)
