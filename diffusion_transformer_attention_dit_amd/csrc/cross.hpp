@@ -42,7 +42,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     long long kh, long long kn_stride, long long oh, long long on_stride, int heads,
     float c2 /* sm_scale * log2(e) */) {
     static_assert(D == 64 || D == 128, "head_dim");
-    constexpr int BN = 64;
+    constexpr int BN = 32;  // keys per tile
     constexpr int KBYTES = BN * D * 2, VBYTES = D * BN * 2;  // LDS bytes of a K / Vt tile
     constexpr int TBYTES = KBYTES + VBYTES;
     constexpr float kLazy = 8.0f;  // rescale only when the max grows by > 2^8
@@ -242,12 +242,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             // Keys past Nk have offsets past the resources: they read as zero.
             const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + h * kh, kv_bytes);
             const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + h * kh, kv_bytes);
-            // Kr fragment f = 2 kb + kk of tile j, straight from the rows:
-            // lane (c, g) gets key 64 j + 32 kk + c, head dims 16 kb + 8 g ..
+            // Kr fragment f = (BN / 32) kb + kk of tile j, straight from the
+            // rows: lane (c, g) gets key BN j + 32 kk + c, head dims
+            // 16 kb + 8 g ..
             for (int F = wave; F < nkv * NKF; F += NW) {
                 const int j = F / NKF, f = F % NKF;
-                const int key = j * BN + (f & 1) * 32 + col;
-                g2lds16(krs, (uint32_t)(((long long)key * kn_stride + (f >> 1) * 16 + half * 8) * 2),
+                const int key = j * BN + (f % (BN / 32)) * 32 + col;
+                g2lds16(krs, (uint32_t)(((long long)key * kn_stride + (f / (BN / 32)) * 16 + half * 8) * 2),
                         smem + j * TBYTES + f * 1024);
             }
             // V rows as they are into tile j's Vt area (row r at byte 2 D r),
@@ -280,13 +281,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // of the tile (the P^T operand order). Tile by tile, every read of a
         // tile's rows before any write of its fragments.
         for (int j = 0; j < nkv; ++j) {
-            constexpr int PER = NVF / NW;  // fragments of a tile per wave
-            static_assert(NVF % NW == 0, "Vt fragments per wave");
+            constexpr int PER = (NVF + NW - 1) / NW;  // fragments of a tile per wave, at most
             char* vt_tile = smem + j * TBYTES + KBYTES;
             uint4 vf[PER];
 #pragma unroll
             for (int i = 0; i < PER; ++i) {
                 const int g4 = i * NW + wave, kq = g4 % (BN / 16);
+                if (g4 >= NVF) break;
                 const char* raw = vt_tile + ((g4 / (BN / 16)) * 32 + col) * 2;
                 uint32_t w[4];
 #pragma unroll
@@ -301,7 +302,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < PER; ++i)
-                *reinterpret_cast<uint4*>(vt_tile + (i * NW + wave) * 1024 + lane * 16) = vf[i];
+                if (i * NW + wave < NVF)
+                    *reinterpret_cast<uint4*>(vt_tile + (i * NW + wave) * 1024 + lane * 16) = vf[i];
         }
         __syncthreads();
 
