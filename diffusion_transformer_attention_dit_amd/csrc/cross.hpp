@@ -28,9 +28,9 @@ constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 // A unit is 32 query rows of one head (one wave's share), units numbered
 // head-major. Each workgroup takes a contiguous range of units (below): for
 // each head in that range it copies the head's context to LDS in the
-// Kr / Vt fragment layout of rope_k_vt_kernel (K gathered by the copies
-// themselves, V copied row by row and transposed in LDS), then its waves
-// take the head's units in turn, each unit
+// Kr / Vt fragment layout of rope_k_vt_kernel, in tiles of 32 keys (K
+// gathered by the copies themselves, V copied row by row and transposed in
+// LDS), then its waves take the head's units in turn, each unit
 // independently: Q to registers (two units' Q loads kept in flight ahead of
 // the one computing), S^T = K Q^T and online softmax over the key tiles
 // exactly as in attn_fwd_kernel, O^T = V^T P^T, O / l stored.
@@ -125,8 +125,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
         for (int j = 0; j < nkv; ++j) {
             const char* ks = smem + j * TBYTES;
-            // Fragments as in attn_fwd_kernel: 0..NK-1 the Kr tile, then the
-            // Vt tile, 1 KiB each, lane l's part at 16 l.
+            // Fragments: 0..NK-1 the Kr tile, then the Vt tile, 1 KiB each,
+            // lane l's part at 16 l (the layout of rope_k_vt_kernel, for
+            // BN-key tiles).
             constexpr int KB = D / 16, NK = (BN / 32) * KB, QB16 = BN / 16, NV = (D / 32) * QB16;
             auto frag = [&](int f) -> bf16x8 {
                 return *reinterpret_cast<const bf16x8*>(ks + f * 1024 + lane * 16);
