@@ -1,10 +1,10 @@
 // Cross-attention of regen_attn to a short conditioning context (CDNA4,
-// gfx950). A DiT block attends to the text / image encoder's tokens besides
-// its own (blog summary, "Methodology - deep read": the encoders condition
-// the decoder); with a context of at most kCrossMaxKeys tokens the whole
-// context of one head fits in LDS, so each workgroup copies it there once
-// and its waves stream query rows against it with no barrier between them.
-// The call is then bound by reading Q and writing O from and to HBM.
+// gfx950). A DiT block attends to the conditioning encoders' tokens besides
+// its own (blog summary, "Methodology - deep read", names the decoder's CLIP
+// and T5 conditioning encoders); with a context of at most kCrossMaxKeys
+// tokens the whole context of one head fits in LDS, so each workgroup copies
+// it there once and its waves stream query rows against it with no barrier
+// between them. Reading Q and writing O from and to HBM is the floor.
 #pragma once
 
 #include "attention.hpp"
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // points are then fixed, and each wait below names exactly what it needs.
     constexpr int QL = D / 16;                 // Q loads per unit
     constexpr int ST = D / 8 + (LSE ? 1 : 0);  // stores per unit
-    constexpr uint32_t kOut = 0x80000000u;     // an offset past every resource
+    constexpr uint32_t kOut = 0x80000000u;     // past every resource (the host keeps them < 2^31 bytes)
     const uint32_t q_bytes = (uint32_t)(((long long)(Nq - 1) * qn_stride + D) * 2);
     const uint32_t o_bytes = (uint32_t)(((long long)(Nq - 1) * on_stride + D) * 2);
     // This lane's half-row of the Q rows of unit uu (zero past Nq or when

@@ -409,7 +409,11 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
     };
 
     // A short context stays in LDS: one kernel, one pass over the queries.
-    const bool short_ctx = cross && nk <= regen::kCrossMaxKeys && nk * kn * 2 < (int64_t(1) << 31);
+    // Its buffer resources take byte offsets below 2^31 into one head of q,
+    // o, lse and the context (2^31 marks an access to drop).
+    const int64_t span_q = ((nq - 1) * std::max(qn, on) + p.head_dim) * 2;
+    const bool short_ctx = cross && nk <= regen::kCrossMaxKeys && nk * kn * 2 < (int64_t(1) << 31) &&
+                           span_q < (int64_t(1) << 31) && nq * 4 < (int64_t(1) << 31);
     const int64_t cross_units = int64_t(p.heads) * ((nq + 31) / 32);
     const dim3 cgrid{unsigned(std::min<int64_t>(h->Pc, cross_units)), 1u, 1u};
     if (short_ctx) {
