@@ -594,15 +594,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // ---------------------------------------------------------------------------
-// merge_kernel: merge of split leftover tiles. Grid (rem tiles, BM MW / 4),
-// 256 threads: MW waves (1 or 4) per query row, D/64 head dims per lane. A
-// tile held whole by one workgroup returns at once. For row r over the
-// segments s holding it:
+// merge_kernel: merge of split leftover tiles. Grid (rem tiles, BM / RPB),
+// 256 threads. A tile held whole by one workgroup returns at once. For row r
+// over the segments s holding it:
 //   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 //   lse = ln 2 (M + log2 sum_s 2^(m_s - M) l_s).
-// Wave w of a row folds segments w, w + MW, ... in one pass with a running
-// maximum; with MW = 4 the four partial results are then folded the same
-// way (tiles split many ways), with MW = 1 a wave takes the whole row (few).
+// MW = 4 (tiles split many ways): four waves per row (RPB = 1), D/64 head
+// dims per lane; wave w folds segments w, w + 4, ... in one pass with a
+// running maximum, then the four partial results are folded the same way.
+// MW = 1 (tiles split a few ways): 16 lanes per row, D/16 head dims per lane
+// (16- or 32-byte loads), four rows per wave (RPB = 16); each lane folds all
+// of its row's segments.
 // ---------------------------------------------------------------------------
 template <int D, int NW, int MW>
 __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -610,16 +612,20 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
                                                     const float* __restrict__ part_ml, int N,
                                                     Sched sc, long long oh, long long on_stride) {
     constexpr int BM = NW * 32;
-    constexpr int DPL = D / 64;  // head dims per lane (2 or 1)
     static_assert(MW == 1 || MW == 4, "waves per row");
+    constexpr int LPR = MW == 4 ? 64 : 16;    // lanes per row (of one wave)
+    constexpr int DPL = D / LPR;              // head dims per lane
+    constexpr int RPB = MW == 4 ? 1 : 16;     // rows per block
     const long long t = (long long)sc.full * sc.P + blockIdx.x;
     const long long y0 = (long long)blockIdx.x * sc.nkv;  // leftover unit offsets of tile t
     const int p0 = rem_owner(sc, y0);
     const int p1 = rem_owner(sc, y0 + sc.nkv - 1);
     if (p0 == p1) return;  // uniform over the block
     const int hd = (int)(t / sc.n_qtiles), qt = (int)(t % sc.n_qtiles);
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r = blockIdx.y * (4 / MW) + wv / MW, w = wv % MW;
+    const int wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & (LPR - 1);
+    const int r = MW == 4 ? blockIdx.y : blockIdx.y * RPB + (threadIdx.x >> 4);
+    const int w = MW == 4 ? wv : 0;
     const int qrow = qt * BM + r;
     if (qrow >= N) return;  // uniform over the block when MW == 4
 
@@ -636,12 +642,15 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
         const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((size_t)slot * BM + r) * 2);
         const float* po = part_o + ((size_t)slot * BM + r) * D + lane * DPL;
         float x[DPL];
-        if constexpr (DPL == 2) {
-            const float2 v = *reinterpret_cast<const float2*>(po);
-            x[0] = v.x;
-            x[1] = v.y;
-        } else {
+        if constexpr (DPL == 1) {
             x[0] = po[0];
+        } else {
+#pragma unroll
+            for (int i = 0; i < DPL; i += 2) {
+                const float2 v = *reinterpret_cast<const float2*>(po + i);
+                x[i] = v.x;
+                x[i + 1] = v.y;
+            }
         }
         const float Mn = fmaxf(M, ml.x);
         const float a = __builtin_amdgcn_exp2f(M - Mn), b = __builtin_amdgcn_exp2f(ml.x - Mn);
@@ -681,11 +690,17 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
     const float inv = 1.0f / Lt;
     if (lse != nullptr && lane == 0) lse[(size_t)hd * N + qrow] = (Mt + log2f(Lt)) * 0.69314718055994531f;
     uint16_t* op = o + hd * oh + qrow * on_stride + lane * DPL;
-    if constexpr (DPL == 2) {
-        *reinterpret_cast<uint32_t*>(op) = pack_bf16(at[0] * inv, at[1] * inv);
+    uint32_t pk[DPL > 1 ? DPL / 2 : 1];
+#pragma unroll
+    for (int i = 0; i < DPL / 2; ++i) pk[i] = pack_bf16(at[2 * i] * inv, at[2 * i + 1] * inv);
+    if constexpr (DPL == 8) {
+        *reinterpret_cast<uint4*>(op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else if constexpr (DPL == 4) {
+        *reinterpret_cast<uint2*>(op) = make_uint2(pk[0], pk[1]);
+    } else if constexpr (DPL == 2) {
+        *reinterpret_cast<uint32_t*>(op) = pk[0];
     } else {
-        const uint32_t w2 = pack_bf16(at[0] * inv, 0.0f);
-        *op = (uint16_t)(w2 & 0xffffu);
+        *op = (uint16_t)(pack_bf16(at[0] * inv, 0.0f) & 0xffffu);
     }
 }
 

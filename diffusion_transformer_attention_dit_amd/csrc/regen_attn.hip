@@ -377,7 +377,7 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
     sc.Prem = int(sc.rem_units < h->P ? (sc.rem_units > 0 ? sc.rem_units : 1) : h->P);
     // Tiles split many ways merge with 4 waves per row, others with one.
     const bool mw4 = sc.Prem >= 8 * rem_tiles;
-    const dim3 mgrid{unsigned(rem_tiles), unsigned(mw4 ? kBM : kBM / 4), 1u};
+    const dim3 mgrid{unsigned(rem_tiles), unsigned(mw4 ? kBM : kBM / 16), 1u};
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
     const uint16_t* k16 = static_cast<const uint16_t*>(k);
     const uint16_t* v16 = static_cast<const uint16_t*>(v);
