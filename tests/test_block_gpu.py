@@ -72,6 +72,24 @@ def test_linear_against_fp64(rows, fin, fout):
     assert err.sum() / np.abs(ref).sum() <= 3e-3
 
 
+def test_linear_window_qkv_shape_sampled_rows():
+    # The QKV projection at the 25-frame window's size (10920 x 1536 -> 4608:
+    # 3096 tiles, 24 of them as quarter tiles), checked on sampled rows.
+    rows, fin, fout = 10920, 1536, 4608
+    say("case linear rows=%d in=%d out=%d (sampled rows)" % (rows, fin, fout))
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(rows, fin, generator=g).to(torch.bfloat16)
+    w = (torch.randn(fout, fin, generator=g) * fin ** -0.5).to(torch.bfloat16)
+    y = native.linear(x.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    pick = synth.sample_rows(rows, 384, seed=3)
+    ref = x.double().numpy()[pick] @ w.double().numpy().T
+    got = f64(y)[pick]
+    err = np.abs(got - ref)
+    assert err.max() <= 2 ** -8 * np.abs(ref).max() + 1e-4, err.max()
+    assert err.sum() / np.abs(ref).sum() <= 3e-3
+
+
 @pytest.mark.skip(reason="this case (the 10920-token block, formerly with hipBLASLt projections) "
                          "faulted the GPU and its cause was not shown; it stays off the GPU")
 def test_block_window_sampled_rows():
