@@ -143,4 +143,150 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict
     }
 }
 
+// ---------------------------------------------------------------------------
+// gemm_nt256_kernel: the same product for large outputs, persistent. G
+// workgroups of 8 waves (one per CU: 128 KiB of LDS). The output is cut into
+// 256 x 256 tiles (64 x 128 per wave, 2 x 4 MFMA blocks, K steps of 64,
+// double-buffered LDS-DMA copies as above); workgroup p computes tiles
+// p, p + G, ... of the first `rounds` G tiles, then the remaining tiles as
+// 128 x 64 eighths (32 x 32 per wave) when they fit in one round, else as
+// 128 x 128 quarters (32 x 64 per wave), quarter q to workgroup q mod G.
+// Tiles are numbered in groups of 4 tile rows as in gemm_nt_kernel, and the
+// workgroups of one XCD take consecutive numbers.
+// ---------------------------------------------------------------------------
+constexpr int kGemmBig = 256;
+constexpr int kGemmBigSmem = 2 * 2 * kGemmBig * kGemmBK * 2;  // [buffer][A, B] at 256 rows
+
+// Copies of ROWS rows x 64 k of a tile (ROWS / 8 runs of 1 KiB over 8 waves).
+template <int ROWS>
+__device__ __forceinline__ void gemm8_issue(__amdgpu_buffer_rsrc_t rs, int ld, int row0, int k0, char* lds,
+                                            int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < ROWS / 64; ++i) {
+        const int run = i * 8 + wave;
+        const int p = run * 64 + lane;
+        const int r = p >> 3, pc = p & 7;
+        const int c = pc ^ ((r >> 1) & 7);
+        g2lds16(rs, (uint32_t)(((long long)(row0 + r) * ld + k0 + c * 8) * 2), lds + run * 1024);
+    }
+}
+
+// One (4 WTM) x (2 WTN) tile at (m0, n0) by 8 waves (WTM x WTN each). Ends
+// with every wave past its last read of `smem`.
+template <int WTM, int WTN>
+__device__ __forceinline__ void gemm8_tile(__amdgpu_buffer_rsrc_t ra, int lda, __amdgpu_buffer_rsrc_t rb,
+                                           int ldb, uint16_t* __restrict__ C, int ldc, int M, int N, int K,
+                                           int m0, int n0, char* smem) {
+    constexpr int TM = 4 * WTM, TN = 2 * WTN, NBM = WTM / 32, NBN = WTN / 32;
+    constexpr int ABYTES = TM * kGemmBK * 2, SBYTES = (TM + TN) * kGemmBK * 2;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 31, half = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1;
+    f32x16 acc[NBM][NBN];
+#pragma unroll
+    for (int i = 0; i < NBM; ++i)
+#pragma unroll
+        for (int j = 0; j < NBN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    gemm8_issue<TM>(ra, lda, m0, 0, smem, wave, lane);
+    gemm8_issue<TN>(rb, ldb, n0, 0, smem + ABYTES, wave, lane);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int nk = K / kGemmBK;
+    for (int kt = 0; kt < nk; ++kt) {
+        char* cur = smem + (kt & 1) * SBYTES;
+        if (kt + 1 < nk) {
+            char* nxt = smem + ((kt + 1) & 1) * SBYTES;
+            gemm8_issue<TM>(ra, lda, m0, (kt + 1) * kGemmBK, nxt, wave, lane);
+            gemm8_issue<TN>(rb, ldb, n0, (kt + 1) * kGemmBK, nxt + ABYTES, wave, lane);
+        }
+        const char* as = cur;
+        const char* bs = cur + ABYTES;
+#pragma unroll
+        for (int kk = 0; kk < kGemmBK / 16; ++kk) {
+            bf16x8 a[NBM], b[NBN];
+#pragma unroll
+            for (int i = 0; i < NBM; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(as + swz_off<128>(wm * WTM + i * 32 + col, kk * 2 + half));
+#pragma unroll
+            for (int j = 0; j < NBN; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(bs + swz_off<128>(wn * WTN + j * 32 + col, kk * 2 + half));
+#pragma unroll
+            for (int i = 0; i < NBM; ++i)
+#pragma unroll
+                for (int j = 0; j < NBN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+        }
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    const bool st8 = (ldc & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < NBM; ++i) {
+        const int m = m0 + wm * WTM + i * 32 + col;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < NBN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WTN + j * 32 + g * 8 + half * 4;
+                const f32x16& v = acc[i][j];
+                uint16_t* cp = C + (long long)m * ldc + n;
+                if (st8 && n + 3 < N) {
+                    *reinterpret_cast<uint2*>(cp) = make_uint2(pack_bf16(v[g * 4], v[g * 4 + 1]),
+                                                               pack_bf16(v[g * 4 + 2], v[g * 4 + 3]));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) cp[e] = (uint16_t)(pack_bf16(v[g * 4 + e], 0.0f) & 0xffffu);
+                }
+            }
+    }
+}
+
+__global__ __launch_bounds__(512) void gemm_nt256_kernel(const uint16_t* __restrict__ A, int lda,
+                                                         const uint16_t* __restrict__ B, int ldb,
+                                                         uint16_t* __restrict__ C, int ldc, int M, int N,
+                                                         int K, int rounds) {
+    __shared__ __attribute__((aligned(1024))) char smem[kGemmBigSmem];
+    constexpr int GM = 4;
+    const int G = gridDim.x;
+    const int pid = xcd_remap(blockIdx.x, G);
+    const int mt = (M + kGemmBig - 1) / kGemmBig, nt = (N + kGemmBig - 1) / kGemmBig;
+    const int tiles = mt * nt;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)((long long)M * lda * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)((long long)N * ldb * 2));
+    auto origin = [&](int t, int* m0, int* n0) {
+        const int first = (t / (GM * nt)) * GM;
+        const int gm = min(mt - first, GM);
+        const int r = t - first * nt;
+        *m0 = (first + r % gm) * kGemmBig;
+        *n0 = (r / gm) * kGemmBig;
+    };
+    for (int k = 0; k < rounds; ++k) {
+        int m0, n0;
+        origin(k * G + pid, &m0, &n0);
+        gemm8_tile<64, 128>(ra, lda, rb, ldb, C, ldc, M, N, K, m0, n0, smem);
+    }
+    const int done = rounds * G, left = tiles - done;
+    if (left * 8 <= G) {
+        // Eighths (128 x 64, 32 x 32 per wave) when they fit in one round.
+        if (pid < left * 8) {
+            int m0, n0;
+            origin(done + pid / 8, &m0, &n0);
+            gemm8_tile<32, 32>(ra, lda, rb, ldb, C, ldc, M, N, K, m0 + ((pid & 7) >> 2) * 128,
+                               n0 + (pid & 3) * 64, smem);
+        }
+        return;
+    }
+    for (int qd = pid; qd < left * 4; qd += G) {
+        int m0, n0;
+        origin(done + qd / 4, &m0, &n0);
+        gemm8_tile<32, 64>(ra, lda, rb, ldb, C, ldc, M, N, K, m0 + ((qd & 3) >> 1) * 128,
+                           n0 + (qd & 1) * 128, smem);
+    }
+}
+
 }  // namespace regen

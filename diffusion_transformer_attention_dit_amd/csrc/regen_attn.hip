@@ -707,12 +707,15 @@ void block_free(regen_block* b) {
     delete b;
 }
 
-// Resident gemm_nt_kernel workgroups per device (CUs x workgroups per CU),
-// queried once per device.
+// Resident workgroups per device of gemm_nt_kernel and gemm_nt256_kernel
+// (CUs x workgroups per CU), queried once per device.
+struct GemmSlots {
+    int small, big;
+};
 std::mutex g_gemm_mu;
-std::unordered_map<int, int> g_gemm_slots;
+std::unordered_map<int, GemmSlots> g_gemm_slots;
 
-regen_status gemm_slots(int* slots) {
+regen_status gemm_slots(GemmSlots* slots) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
@@ -722,22 +725,36 @@ regen_status gemm_slots(int* slots) {
         *slots = it->second;
         return REGEN_OK;
     }
-    int cus = 0, per_cu = 0;
+    int cus = 0, per_cu = 0, per_cu_big = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
         return fail_hip(e, "hipDeviceGetAttribute");
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, regen::gemm_nt_kernel, 256, 0)) !=
-        hipSuccess)
+            hipSuccess ||
+        (e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_big, regen::gemm_nt256_kernel, 512, 0)) !=
+            hipSuccess)
         return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-    *slots = std::max(1, cus) * std::max(1, per_cu);
+    slots->small = std::max(1, cus) * std::max(1, per_cu);
+    slots->big = std::max(1, cus) * std::max(1, per_cu_big);
     g_gemm_slots[dev] = *slots;
     return REGEN_OK;
 }
 
 regen_status gemm(const uint16_t* A, int lda, const uint16_t* B, int ldb, uint16_t* C, int ldc, int M,
                   int N, int K, hipStream_t st) {
-    int slots = 1;
-    const regen_status s = gemm_slots(&slots);
+    GemmSlots sl{1, 1};
+    const regen_status s = gemm_slots(&sl);
     if (s != REGEN_OK) return s;
+    // At least one full round of 256 x 256 tiles: the persistent kernel.
+    const int64_t big_tiles = int64_t((M + regen::kGemmBig - 1) / regen::kGemmBig) *
+                              ((N + regen::kGemmBig - 1) / regen::kGemmBig);
+    if (big_tiles >= sl.big && big_tiles * 4 <= INT32_MAX) {
+        hipLaunchKernelGGL(regen::gemm_nt256_kernel, dim3(unsigned(sl.big)), dim3(512), 0, st, A, lda, B,
+                           ldb, C, ldc, M, N, K, int(big_tiles / sl.big));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail_hip(e, "gemm_nt256_kernel launch");
+        return REGEN_OK;
+    }
+    const int slots = sl.small;
     const int64_t tiles = int64_t((M + regen::kGemmTile - 1) / regen::kGemmTile) *
                           ((N + regen::kGemmTile - 1) / regen::kGemmTile);
     // Quarter tiles for a short last round: only after at least one full

@@ -56,6 +56,10 @@ def test_block_all_elements(name):
     # 33 x 16 = 528 tiles of 128 x 128: one full round on 256 CUs x 2, the
     # last 16 tiles (ragged rows and columns among them) as 64 x 64 quarters
     (4100, 256, 2000),
+    # 17 x 17 = 289 tiles of 256 x 256 (persistent kernel): one round, the
+    # other 33 (ragged ones among them) as 128 x 128 quarters; 10920 x 1536
+    # -> 1536 above leaves 2 of 258 as 128 x 64 eighths
+    (4100, 256, 4100),
 ])
 def test_linear_against_fp64(rows, fin, fout):
     say("case linear rows=%d in=%d out=%d" % (rows, fin, fout))
