@@ -88,6 +88,25 @@ def test_cross_head_dim_64(ctx_len):
     assert d.max() <= 2e-2 and d.mean() <= 2e-3, (d.max(), d.mean())
 
 
+def test_cross_more_heads_than_workgroups():
+    # 300 heads of 32 tokens: fewer workgroups than heads, so each workgroup
+    # of the short-context kernel takes whole heads, one context after another.
+    heads, grid, ctx = 300, (1, 4, 8), 20
+    say("case cross-attention, %d heads x %d tokens, ctx %d" % (heads, 32, ctx))
+    g = torch.Generator().manual_seed(23)
+    q = (torch.randn(heads, 32, 64, generator=g) * 0.5).to(torch.bfloat16)
+    kc = (torch.randn(heads, ctx, 64, generator=g) * 0.5).to(torch.bfloat16)
+    vc = (torch.randn(heads, ctx, 64, generator=g) * 0.5).to(torch.bfloat16)
+    attn = native.Attention(heads, 64, grid)
+    o, lse = attn.forward_cross(q.cuda(), kc.cuda(), vc.cuda(), lse=None)
+    torch.cuda.synchronize()
+    attn.close()
+    ref_o, ref_lse = oracle.c_attention(f64(q), f64(kc), f64(vc), return_lse=True)
+    check_o(f64(o), ref_o, "cross 300 heads")
+    d = np.abs(lse.cpu().double().numpy() - ref_lse)
+    assert d.max() <= 2e-2 and d.mean() <= 2e-3, (d.max(), d.mean())
+
+
 def test_cross_token_major_matches_head_major():
     w = synth.WORKLOADS["block_12x128_n1560"]
     say("case cross-attention token-major")
