@@ -3,6 +3,7 @@ the header declares, and rejects bad arguments before touching a device."""
 import ctypes
 import os
 import re
+import sys
 
 import pytest
 import torch
@@ -184,3 +185,15 @@ def test_linear_argument_checks_before_the_device():
     if not torch.cuda.is_available():
         assert native.regen_linear(0x100000, 0x200000, 0x300000, 4, 64, 8, None) == \
             native.REGEN_ERR_NO_DEVICE
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # The library has no multi-GPU path: bench.py says so and exits non-zero
+    # before touching any device.
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
