@@ -16,17 +16,19 @@ from .native import Attention
 class WindowDriver:
     """Holds the library handle, the pre-drawn inputs of every call of one
     window and a pair of output buffers (alternating, as consecutive blocks
-    would)."""
+    would), or one output per call with keep_outputs (for checking every
+    call of a window)."""
 
     def __init__(self, workload: synth.Workload, device="cuda", base_seed=0, steps=None,
-                 blocks=None):
+                 blocks=None, keep_outputs=False):
         self.w = workload
         self.steps = steps if steps is not None else workload.steps
         self.blocks = blocks if blocks is not None else workload.blocks
         self.attn = Attention(workload.heads, workload.head_dim, workload.grid)
         self.inputs = [synth.make_qkv(workload, s, b, device=device, base_seed=base_seed)
                        for s in range(self.steps) for b in range(self.blocks)]
-        self.outs = [torch.empty_like(self.inputs[0][0]) for _ in range(2)]
+        self.keep = bool(keep_outputs)
+        self.outs = [torch.empty_like(self.inputs[0][0]) for _ in range(self.calls if self.keep else 2)]
 
     @property
     def calls(self):
@@ -39,10 +41,12 @@ class WindowDriver:
     def run_window(self, stream=None):
         """Enqueue all steps x blocks attention calls on one stream."""
         for i, (q, k, v) in enumerate(self.inputs):
-            self.attn.forward(q, k, v, out=self.outs[i & 1], stream=stream)
+            self.attn.forward(q, k, v, out=self.outs[i if self.keep else i & 1], stream=stream)
 
     def output_of(self, call):
-        return self.outs[call & 1]
+        """The output of call `call` of the last window (with the default two
+        buffers, valid for the last two calls only)."""
+        return self.outs[call if self.keep else call & 1]
 
     def close(self):
         self.attn.close()

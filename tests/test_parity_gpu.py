@@ -125,6 +125,31 @@ def test_full_size_sampled_rows(name, step, block, rows):
     assert (of >= vf.amin(dim=1, keepdim=True) - 1e-2).all()
 
 
+def test_window_driver_every_call():
+    # The four-step window driver: 4 steps x 30 blocks = 120 calls on one
+    # stream, each on its own seeded inputs. Every call's output is finite
+    # and a convex combination of its V rows; four calls (the first two, one
+    # in the middle, the last) match the oracle on sampled rows.
+    from diffusion_transformer_attention_dit_amd.sampler import WindowDriver
+    w = synth.WORKLOADS["window25_12x128_n10920"]
+    say("case window driver, %d calls" % (w.steps * w.blocks))
+    drv = WindowDriver(w, keep_outputs=True)
+    assert drv.calls == 120
+    drv.run_window()
+    torch.cuda.synchronize()
+    for i in range(drv.calls):
+        of, vf = drv.output_of(i).float(), drv.inputs[i][2].float()
+        assert torch.isfinite(of).all(), i
+        assert (of <= vf.amax(dim=1, keepdim=True) + 1e-2).all(), i
+        assert (of >= vf.amin(dim=1, keepdim=True) - 1e-2).all(), i
+    for i in (0, 1, 61, 119):
+        q, k, v = drv.inputs[i]
+        sample = synth.sample_rows(w.tokens, 24, seed=100 + i)
+        ref = oracle.rope_attention(f64(q), f64(k), f64(v), w.grid, rows=sample)
+        check(f64(drv.output_of(i))[:, sample, :], ref, label="window call %d" % i)
+    drv.close()
+
+
 def test_window_last_tiles_all_rows():
     # The 25-frame window has 12 x 43 = 516 query tiles of 256 rows; on 256
     # resident workgroups the last four (head 11, rows 9984..10919) are split
