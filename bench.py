@@ -246,11 +246,11 @@ def block_leg(w, reps=10):
             "workload": w.name, "ms_per_block": round(t * 1e3, 4), "gflop": round(total / 1e9, 1),
             "tflops": round(total / t / 1e12, 2), "pct_peak": round(100 * total / t / 1e12 / PEAK_BF16_TFLOPS, 2),
             "projection_gflop": round(gemm / 1e9, 1), "attention_gflop": round(w.flops_per_call / 1e9, 1),
-            "qkv_projection_window": {"kernel": "gemm_nt_kernel", "shape": [window.tokens, hid, 3 * hid],
+            "qkv_projection_window": {"kernel": "gemm_nt256_kernel", "shape": [window.tokens, hid, 3 * hid],
                                       "avg_launch_us": round(tg * 1e6, 2), "bound": "mfma",
                                       "achieved": round(gf / tg / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
                                       "unit": "TFLOP/s", "frac": round(gf / tg / 1e12 / PEAK_BF16_TFLOPS, 4)},
-            "o_projection_window": {"kernel": "gemm_nt_kernel", "shape": [window.tokens, hid, hid],
+            "o_projection_window": {"kernel": "gemm_nt256_kernel", "shape": [window.tokens, hid, hid],
                                     "avg_launch_us": round(to * 1e6, 2), "bound": "mfma",
                                     "achieved": round(go / to / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
                                     "unit": "TFLOP/s", "frac": round(go / to / 1e12 / PEAK_BF16_TFLOPS, 4)}}
