@@ -266,7 +266,8 @@ __device__ __forceinline__ bool get_segment(const Sched& sc, int p, int k, long 
 //             token-major view), row m being token q_off + m
 //   Kr, Vt  : the Nk keys prepared by rope_k_vt_kernel (Npad rows per head)
 //   lse     : [heads][Nq] fp32 log-sum-exp of each row's scores, or null
-//   part_o  : [2P][BM][D] fp32 unnormalised O of split tiles
+//   part_o  : [2P][BM][D] bf16 O / l of split tiles (normalised over the
+//             segment's own keys)
 //   part_ml : [2P][BM][2] fp32 (m, l) of split tiles
 // ---------------------------------------------------------------------------
 template <int D, int BN, int NW>
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, float* __restrict__ lse,
     const float2* __restrict__ tab, RopeGeom geo, int Nq, int Nk, int Npad, int q_off,
     long long qh, long long qn_stride, long long oh, long long on_stride, Sched sc,
-    float c2 /* sm_scale * log2(e) */, int rotate_q, float* __restrict__ part_o,
+    float c2 /* sm_scale * log2(e) */, int rotate_q, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml) {
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(BN == 64, "key tile: the Kr / Vt fragment layout holds 64-key tiles");
@@ -550,9 +551,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_half), __float_as_uint(l_half),
                                                    false, false);
         const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const float inv = 1.0f / l_row;
         if (kv0 == 0 && kv1 == sc.nkv) {
             // Whole tile here: O = O^T / l, bf16; lse = ln 2 (m + log2 l).
-            const float inv = 1.0f / l_row;
             if (qrow < Nq) {
                 if (lse != nullptr && half == 0)
                     lse[(size_t)hd * Nq + qrow] = (m_run + log2f(l_row)) * 0.69314718055994531f;
@@ -569,18 +570,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     }
             }
         } else {
-            // Part of a tile: leave (unnormalised O, m, l) for the merge.
+            // Part of a tile: leave (O / l in bf16, m, l) for the merge.
             const int slot = partial_slot(sc, pid, t);
             const int r = wave * 32 + col;
-            float* po = part_o + ((size_t)slot * BM + r) * D;
+            uint16_t* po = part_o + ((size_t)slot * BM + r) * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int d0 = db * 32 + g4 * 8 + half * 4;
-                    *reinterpret_cast<float4*>(po + d0) =
-                        make_float4(acc[db][g4 * 4 + 0], acc[db][g4 * 4 + 1], acc[db][g4 * 4 + 2],
-                                    acc[db][g4 * 4 + 3]);
+                    uint2 w2;
+                    w2.x = pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv);
+                    w2.y = pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv);
+                    *reinterpret_cast<uint2*>(po + d0) = w2;
                 }
             if (half == 0)
                 *reinterpret_cast<float2*>(part_ml + ((size_t)slot * BM + r) * 2) = make_float2(m_run, l_row);
@@ -596,19 +598,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // ---------------------------------------------------------------------------
 // merge_kernel: merge of split leftover tiles. Grid (rem tiles, BM / RPB),
 // 256 threads. A tile held whole by one workgroup returns at once. For row r
-// over the segments s holding it:
-//   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// over the segments s holding it (segment s left O_s / l_s in bf16):
+//   M = max_s m_s,  O = sum_s 2^(m_s - M) l_s (O_s / l_s) / sum_s 2^(m_s - M) l_s,
 //   lse = ln 2 (M + log2 sum_s 2^(m_s - M) l_s).
 // MW = 4 (tiles split many ways): four waves per row (RPB = 1), D/64 head
 // dims per lane; wave w folds segments w, w + 4, ... in one pass with a
 // running maximum, then the four partial results are folded the same way.
 // MW = 1 (tiles split a few ways): 16 lanes per row, D/16 head dims per lane
-// (16- or 32-byte loads), four rows per wave (RPB = 16); each lane folds all
+// (8- or 16-byte loads), four rows per wave (RPB = 16); each lane folds all
 // of its row's segments.
 // ---------------------------------------------------------------------------
 template <int D, int NW, int MW>
 __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, float* __restrict__ lse,
-                                                    const float* __restrict__ part_o,
+                                                    const uint16_t* __restrict__ part_o,
                                                     const float* __restrict__ part_ml, int N,
                                                     Sched sc, long long oh, long long on_stride) {
     constexpr int BM = NW * 32;
@@ -640,21 +642,30 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
     for (int p = p0 + w; p <= p1; p += MW) {
         const int slot = p == p0 ? slot0 : 2 * p;
         const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((size_t)slot * BM + r) * 2);
-        const float* po = part_o + ((size_t)slot * BM + r) * D + lane * DPL;
+        const uint16_t* po = part_o + ((size_t)slot * BM + r) * D + lane * DPL;
         float x[DPL];
         if constexpr (DPL == 1) {
-            x[0] = po[0];
+            x[0] = __uint_as_float((uint32_t)po[0] << 16);
         } else {
+            uint32_t w[DPL / 2];
+            if constexpr (DPL == 8) {
+                const uint4 v = *reinterpret_cast<const uint4*>(po);
+                w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+            } else if constexpr (DPL == 4) {
+                const uint2 v = *reinterpret_cast<const uint2*>(po);
+                w[0] = v.x; w[1] = v.y;
+            } else {
+                w[0] = *reinterpret_cast<const uint32_t*>(po);
+            }
 #pragma unroll
-            for (int i = 0; i < DPL; i += 2) {
-                const float2 v = *reinterpret_cast<const float2*>(po + i);
-                x[i] = v.x;
-                x[i + 1] = v.y;
+            for (int i = 0; i < DPL / 2; ++i) {
+                x[2 * i] = bf_lo(w[i]);
+                x[2 * i + 1] = bf_hi(w[i]);
             }
         }
         const float Mn = fmaxf(M, ml.x);
-        const float a = __builtin_amdgcn_exp2f(M - Mn), b = __builtin_amdgcn_exp2f(ml.x - Mn);
-        L = L * a + b * ml.y;
+        const float a = __builtin_amdgcn_exp2f(M - Mn), b = __builtin_amdgcn_exp2f(ml.x - Mn) * ml.y;
+        L = L * a + b;
 #pragma unroll
         for (int i = 0; i < DPL; ++i) acc[i] = acc[i] * a + b * x[i];
         M = Mn;

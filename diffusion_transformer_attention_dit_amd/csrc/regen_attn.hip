@@ -141,7 +141,7 @@ struct regen_attn {
     uint16_t* d_vt;  // workspace: transposed V
     int P;           // persistent attention workgroups
     int Pc;          // cross_attn_kernel workgroups (one round of resident slots)
-    float* d_part_o;   // split-tile partial O   [2P][BM][D]
+    uint16_t* d_part_o;  // split-tile O / l, bf16 [2P][BM][D]
     float* d_part_ml;  // split-tile (m, l)       [2P][BM][2]
 };
 
@@ -241,7 +241,8 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
     h->geo = geo;
     h->d_tab = h->d_tab_id = nullptr;
     h->d_kr = h->d_vt = nullptr;
-    h->d_part_o = h->d_part_ml = nullptr;
+    h->d_part_o = nullptr;
+    h->d_part_ml = nullptr;
     int per_cu = 1, cross_per_cu = 1;
     s = p.head_dim == 128 ? occupancy<128>(&per_cu, &cross_per_cu) : occupancy<64>(&per_cu, &cross_per_cu);
     if (s != REGEN_OK) {
@@ -262,7 +263,7 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
         if (h->d_part_ml) (void)hipFree(h->d_part_ml);
         delete h;
     };
-    const size_t part_o_bytes = size_t(2) * h->P * kBM * p.head_dim * sizeof(float);
+    const size_t part_o_bytes = size_t(2) * h->P * kBM * p.head_dim * sizeof(uint16_t);
     const size_t part_ml_bytes = size_t(2) * h->P * kBM * 2 * sizeof(float);
     if ((e = hipMalloc(&h->d_tab, 2 * tab_bytes)) != hipSuccess ||
         (e = hipMalloc(&h->d_kr, half_ws)) != hipSuccess ||
