@@ -103,8 +103,9 @@ typedef struct regen_attn *regen_attn_t;
  * 2 * heads * ceil(tokens/128)*128 * head_dim * 2 bytes (rotated K and
  * transposed V; see regen_attn_workspace_size) and a scratch area for query
  * tiles whose keys are split over several workgroups of the persistent
- * attention kernel: 2 * P * 256 * (head_dim + 2) * 4 bytes, P = resident
- * workgroups of the device (one per compute unit on MI355X: 64.5 MiB at
+ * attention kernel: 2 * P * 256 * (2 * head_dim + 8) bytes (bf16 O/l and
+ * fp32 (m, l) per row), P = resident workgroups of the device (one per
+ * compute unit on MI355X: 33 MiB at
  * head_dim 128).
  * On success *out receives the handle; on any failure *out is set to NULL
  * (when out is not NULL) and the status says why:
