@@ -73,16 +73,16 @@ def copy_calibration(mib):
 def counted_traffic(w, algorithmic_bytes):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     passes (FETCH_SIZE, WRITE_SIZE, scaled against a copy of known size), or
-    None when the attention kernels' source (common.hpp + attention.hpp)
-    has changed since they were taken."""
+    None when the attention kernels' source (common.hpp + attention.hpp) or
+    the build flags (build.py) have changed since they were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "attn_fwd_%s_traffic.json" % w.name)
     csrc = os.path.join(ROOT, "diffusion_transformer_attention_dit_amd", "csrc")
     try:
         doc = json.load(open(path))
         h = hashlib.sha256()
-        for name in ("common.hpp", "attention.hpp"):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+        for name in ("csrc/common.hpp", "csrc/attention.hpp", "build.py"):
+            h.update(open(os.path.join(csrc, "..", name), "rb").read())
         sha = h.hexdigest()
     except (OSError, ValueError):
         return None

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libregen_attn.so")
 SOURCES = [os.path.join(CSRC, "regen_attn.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, h) for h in ("common.hpp", "attention.hpp", "gemm.hpp", "layout.hpp")] + \
+DEPENDS = SOURCES + [os.path.join(CSRC, h) for h in ("common.hpp", "attention.hpp", "cross.hpp", "gemm.hpp",
+                                                     "layout.hpp")] + \
     [os.path.join(INCLUDE, "regen_attn.h")]
 
 HIPCC_FLAGS = [
@@ -23,6 +24,9 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
     # Keep packed-FP32 instructions out of the generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The ILP-first iterative scheduler: the attention kernel's loop runs
+    # about 2% faster with it (same instructions, same results).
+    "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
