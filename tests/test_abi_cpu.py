@@ -197,3 +197,14 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_build_tracks_every_kernel_source():
+    # A library older than any of its sources is rebuilt before use, so the
+    # dependency list must name every file under csrc/ and the header.
+    csrc = os.path.join(ROOT, "diffusion_transformer_attention_dit_amd", "csrc")
+    on_disk = {os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".hpp"))}
+    assert on_disk <= set(build.DEPENDS), sorted(on_disk - set(build.DEPENDS))
+    assert os.path.join(ROOT, "include", "regen_attn.h") in build.DEPENDS
+    # Packed FP32 instructions stay out of the generated code.
+    assert "-packed-fp32-ops" in build.HIPCC_FLAGS

@@ -184,6 +184,19 @@ def test_ragged_lengths(grid, head_dim):
     check(f64(o), ref, label="ragged %s" % (grid,))
 
 
+def test_head_dim_64_tiles_split_many_ways():
+    # 2 heads x 1560 tokens at head_dim 64: 14 query tiles of 25 key blocks
+    # shared by all resident workgroups, so every tile is split many ways
+    # and merged by the many-way merge form.
+    grid = (4, 15, 26)
+    say("case head_dim 64, 2 heads x 1560 tokens (many-way split tiles)")
+    q, k, v = synth.make_qkv(synth.WORKLOADS["tiny_1x64_n128"], grid=grid, heads=2, std=0.5)
+    qd, kd, vd = to_dev(q, k, v)
+    o = run_gpu(qd, kd, vd, grid)
+    ref = oracle.rope_attention(f64(qd), f64(kd), f64(vd), grid)
+    check(f64(o), ref, label="head_dim 64, many-way split")
+
+
 def test_no_rope_flag_matches_plain_attention():
     w = synth.WORKLOADS["block_12x128_n1560"]
     say("case NO_ROPE flag")
