@@ -213,49 +213,56 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_
 // blockwise softmax.
 // ---------------------------------------------------------------------------
 struct Sched {
-    int n_qtiles;         // query tiles per head
-    int nkv;              // key blocks per tile
-    int P;                // persistent workgroups
-    int full;             // whole-tile passes
-    int Prem;             // workgroups sharing the leftover units, >= 1
-    long long rem_units;  // units of the leftover tiles (rem * nkv)
+    int n_qtiles;   // query tiles per head
+    int nkv;        // key blocks per tile
+    int P;          // persistent workgroups
+    int full;       // whole-tile passes
+    int Prem;       // workgroups sharing the leftover units, >= 1
+    int rem_units;  // units of the leftover tiles (rem * nkv)
+    int rem_q;      // rem_units / Prem
+    int rem_r;      // rem_units % Prem
 };
+// Every unit index (heads * n_qtiles * nkv) fits in 31 bits (the host checks
+// this), so the schedule runs in 32-bit integer arithmetic.
 
 // Start (offset into the leftover units) of workgroup p's leftover range,
-// p <= Prem; ranges are non-empty because rem_units >= Prem.
-__device__ __forceinline__ long long rem_begin(const Sched& sc, int p) {
-    return (long long)p * sc.rem_units / sc.Prem;
+// p <= Prem: floor(p * rem_units / Prem), split so that no product leaves
+// 32 bits (p * rem_q <= rem_units, p * rem_r < Prem^2). Ranges are non-empty
+// because rem_units >= Prem.
+__host__ __device__ __forceinline__ int rem_begin(const Sched& sc, int p) {
+    return p * sc.rem_q + (p * sc.rem_r) / sc.Prem;
 }
-// The workgroup whose leftover range holds leftover unit y.
-__device__ __forceinline__ int rem_owner(const Sched& sc, long long y) {
-    return (int)(((y + 1) * sc.Prem - 1) / sc.rem_units);
+// The workgroup whose leftover range holds leftover unit y (the largest p
+// with rem_begin(p) <= y). Used by the merge only; 64-bit products.
+__host__ __device__ __forceinline__ int rem_owner(const Sched& sc, int y) {
+    return (int)(((long long)(y + 1) * sc.Prem - 1) / sc.rem_units);
 }
 // Partial-result slot of workgroup p for leftover tile t: the first tile of
 // its range uses 2p, a later (necessarily its last) tile uses 2p + 1.
-__device__ __forceinline__ int partial_slot(const Sched& sc, int p, long long t) {
-    const long long x0 = (long long)sc.full * sc.P * sc.nkv + rem_begin(sc, p);
+__host__ __device__ __forceinline__ int partial_slot(const Sched& sc, int p, int t) {
+    const int x0 = sc.full * sc.P * sc.nkv + rem_begin(sc, p);
     return (t == x0 / sc.nkv) ? 2 * p : 2 * p + 1;
 }
 
 // Segment k of workgroup p's work: tile *t, key blocks [*kv0, *kv1).
 // Returns false past the last segment.
-__device__ __forceinline__ bool get_segment(const Sched& sc, int p, int k, long long* t, int* kv0,
-                                            int* kv1) {
+__host__ __device__ __forceinline__ bool get_segment(const Sched& sc, int p, int k, int* t, int* kv0,
+                                                     int* kv1) {
     if (k < sc.full) {
-        *t = (long long)k * sc.P + p;
+        *t = k * sc.P + p;
         *kv0 = 0;
         *kv1 = sc.nkv;
         return true;
     }
     if (p >= sc.Prem) return false;
-    const long long base = (long long)sc.full * sc.P * sc.nkv;
-    const long long a = base + rem_begin(sc, p), b = base + rem_begin(sc, p + 1);
-    const long long x = (k == sc.full) ? a : (a / sc.nkv + (k - sc.full)) * sc.nkv;
+    const int base = sc.full * sc.P * sc.nkv;
+    const int a = base + rem_begin(sc, p), b = base + rem_begin(sc, p + 1);
+    const int x = (k == sc.full) ? a : (a / sc.nkv + (k - sc.full)) * sc.nkv;
     if (x >= b) return false;
     *t = x / sc.nkv;
-    *kv0 = (int)(x - *t * sc.nkv);
-    const long long left = b - x;
-    *kv1 = (left < (long long)(sc.nkv - *kv0)) ? *kv0 + (int)left : sc.nkv;
+    *kv0 = x - *t * sc.nkv;
+    const int left = b - x;
+    *kv1 = (left < sc.nkv - *kv0) ? *kv0 + left : sc.nkv;
     return true;
 }
 
@@ -296,16 +303,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // Consecutive logical workgroups (hence consecutive tiles of one head)
     // share an XCD and its L2.
     const int pid = xcd_remap(blockIdx.x, gridDim.x);
-    long long t;
-    int kv0, kv1;
+    int t, kv0, kv1;
     if (!get_segment(sc, pid, 0, &t, &kv0, &kv1)) return;  // uniform; no barrier reached yet
 
     const uint32_t head_bytes = (uint32_t)Npad * D * 2;
     const int HW = geo.H * geo.W;
 
     // Buffer resources over the Kr rows and Vt blocks of tile tt's head.
-    auto head_rsrc = [&](long long tt, __amdgpu_buffer_rsrc_t* krs, __amdgpu_buffer_rsrc_t* vrs) {
-        const int h = (int)tt / sc.n_qtiles;
+    auto head_rsrc = [&](int tt, __amdgpu_buffer_rsrc_t* krs, __amdgpu_buffer_rsrc_t* vrs) {
+        const int h = tt / sc.n_qtiles;
         *krs = make_rsrc(kr + (size_t)h * Npad * D, head_bytes);
         *vrs = make_rsrc(vt + (size_t)h * Npad * D, head_bytes);
     };
@@ -315,8 +321,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // bytes (uniform).
     constexpr int QCPR = D / 8;  // 16-byte chunks per Q row
     const bool q_lds = (long long)qn_stride * 2 * BM < (1LL << 31);
-    auto issue_q = [&](long long tt) {
-        const int h = (int)tt / sc.n_qtiles, qtt = (int)tt - h * sc.n_qtiles;
+    auto issue_q = [&](int tt) {
+        const int h = tt / sc.n_qtiles, qtt = tt - h * sc.n_qtiles;
         const int rows = min(BM, Nq - qtt * BM);
         const __amdgpu_buffer_rsrc_t qrs =
             make_rsrc(q + h * qh + (long long)qtt * BM * qn_stride,
@@ -342,12 +348,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     for (int k = 0; more; ++k) {
         // ---- segment k: tile t, key blocks [kv0, kv1) ----
-        long long nt_ = 0;
-        int nkv0 = 0, nkv1 = 0;
+        int nt_ = 0, nkv0 = 0, nkv1 = 0;
         more = get_segment(sc, pid, k + 1, &nt_, &nkv0, &nkv1);
         __amdgpu_buffer_rsrc_t nkrs = krs, nvrs = vrs;  // the next segment's head
         if (more) head_rsrc(nt_, &nkrs, &nvrs);
-        const int hd = (int)t / sc.n_qtiles, qt = (int)t - hd * sc.n_qtiles;
+        const int hd = t / sc.n_qtiles, qt = t - hd * sc.n_qtiles;
         const int qrow = qt * BM + wave * 32 + col;
 
         // Q: load this lane's half-rows, rotate them (RoPE on load) and fold
@@ -453,14 +458,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
             __builtin_amdgcn_s_setprio(0);
             // Keys past the end of the sequence get -inf (never zero-padding).
+            // The number of this lane's valid keys is made opaque to the
+            // compiler, which would otherwise hoist the 32 comparisons out of
+            // the loop and keep their lane masks in 64 scalar registers.
             if (b == sc.nkv - 1 && (Nk % BN) != 0) {
+                int left = Nk - b * BN - half * 4;  // keys of this lane's row left in the block
+                __asm__ volatile("" : "+v"(left));
 #pragma unroll
                 for (int kk = 0; kk < BN / 32; ++kk)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = b * BN + kk * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-                        if (key >= Nk) s[kk][i] = -INFINITY;
-                    }
+                    for (int i = 0; i < 16; ++i)
+                        if (kk * 32 + (i / 4) * 8 + (i % 4) >= left) s[kk][i] = -INFINITY;
             }
 
             // Row max of s: in-lane over this lane's keys (4 independent
@@ -618,12 +626,12 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
     constexpr int LPR = MW == 4 ? 64 : 16;    // lanes per row (of one wave)
     constexpr int DPL = D / LPR;              // head dims per lane
     constexpr int RPB = MW == 4 ? 1 : 16;     // rows per block
-    const long long t = (long long)sc.full * sc.P + blockIdx.x;
-    const long long y0 = (long long)blockIdx.x * sc.nkv;  // leftover unit offsets of tile t
+    const int t = sc.full * sc.P + blockIdx.x;
+    const int y0 = blockIdx.x * sc.nkv;  // leftover unit offsets of tile t
     const int p0 = rem_owner(sc, y0);
     const int p1 = rem_owner(sc, y0 + sc.nkv - 1);
     if (p0 == p1) return;  // uniform over the block
-    const int hd = (int)(t / sc.n_qtiles), qt = (int)(t % sc.n_qtiles);
+    const int hd = t / sc.n_qtiles, qt = t % sc.n_qtiles;
     const int wv = threadIdx.x >> 6;
     const int lane = threadIdx.x & (LPR - 1);
     const int r = MW == 4 ? blockIdx.y : blockIdx.y * RPB + (threadIdx.x >> 4);

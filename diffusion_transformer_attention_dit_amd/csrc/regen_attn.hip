@@ -113,6 +113,11 @@ regen_status resolve(const regen_attn_desc* d, Problem* p) {
     p->n_qtiles = int((tokens + kBM - 1) / kBM);
     p->nkv = int((tokens + kBN - 1) / kBN);
     p->units = int64_t(p->heads) * p->n_qtiles * p->nkv;
+    // The attention schedule numbers (query tile, key block) pairs in 31 bits.
+    if (p->units >= (int64_t(1) << 31))
+        return fail(REGEN_ERR_INVALID_ARGUMENT,
+                    "too many (query tile, key block) pairs: heads * ceil(tokens/256) * "
+                    "ceil(tokens/64) must stay below 2^31");
     return REGEN_OK;
 }
 
@@ -350,6 +355,25 @@ regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, 
     return enqueue(h, q, q_begin, nq, k, v, kv_begin, nk, o, lse, stream, cross, sd);
 }
 
+// Schedule of the persistent attention kernel over P workgroups for one
+// call (see regen::Sched). False if the call's unit count needs more than
+// 31 bits.
+bool make_sched(int heads, int64_t nq, int64_t nk, int P, regen::Sched* sc, int64_t* rem_tiles) {
+    const int64_t n_qtiles = (nq + kBM - 1) / kBM, nkv = (nk + kBN - 1) / kBN;
+    const int64_t tiles = int64_t(heads) * n_qtiles;
+    if (tiles * nkv >= (int64_t(1) << 31)) return false;
+    sc->n_qtiles = int(n_qtiles);
+    sc->nkv = int(nkv);
+    sc->P = P;
+    sc->full = int(tiles / P);
+    *rem_tiles = tiles - int64_t(sc->full) * P;
+    sc->rem_units = int(*rem_tiles * nkv);
+    sc->Prem = sc->rem_units < P ? (sc->rem_units > 0 ? sc->rem_units : 1) : P;
+    sc->rem_q = sc->rem_units / sc->Prem;
+    sc->rem_r = sc->rem_units % sc->Prem;
+    return true;
+}
+
 // Enqueue the kernels of one call whose arguments have been checked.
 regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, const void* k,
                      const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse,
@@ -368,14 +392,11 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
 
     dim3 pgrid(unsigned(Npad / regen::kPrepBlock), unsigned(p.heads));
     regen::Sched sc;
-    sc.n_qtiles = int((nq + kBM - 1) / kBM);
-    sc.nkv = int((nk + kBN - 1) / kBN);
-    const int64_t tiles = int64_t(p.heads) * sc.n_qtiles;
-    sc.P = h->P;
-    sc.full = int(tiles / h->P);
-    const int64_t rem_tiles = tiles - int64_t(sc.full) * h->P;
-    sc.rem_units = rem_tiles * sc.nkv;
-    sc.Prem = int(sc.rem_units < h->P ? (sc.rem_units > 0 ? sc.rem_units : 1) : h->P);
+    int64_t rem_tiles = 0;
+    if (!make_sched(p.heads, nq, nk, h->P, &sc, &rem_tiles))
+        return fail(REGEN_ERR_INVALID_ARGUMENT,
+                    "too many (query tile, key block) pairs for one call (heads * ceil(q/256) * "
+                    "ceil(k/64) must stay below 2^31)");
     // Tiles split many ways merge with 4 waves per row, others with one.
     const bool mw4 = sc.Prem >= 8 * rem_tiles;
     const dim3 mgrid{unsigned(rem_tiles), unsigned(mw4 ? kBM : kBM / 16), 1u};

@@ -90,8 +90,15 @@ def test_one_head_key_workspace_limit():
     s, h = native.regen_attn_create(over)
     assert s == native.REGEN_ERR_INVALID_ARGUMENT and h is None
     assert "one head" in native.regen_attn_last_error()
-    under = good_desc(heads=1, grid=(127, 256, 256))
-    assert native.regen_attn_workspace_size(under) == 2 * 127 * 256 * 256 * 128 * 2
+    # Below it, the schedule's 31-bit numbering of (query tile, key block)
+    # pairs is the binding limit: heads * ceil(N/256) * ceil(N/64) < 2^31.
+    under = good_desc(heads=1, grid=(90, 256, 256))  # 23040 x 92160 pairs
+    assert native.regen_attn_workspace_size(under) == 2 * 90 * 256 * 256 * 128 * 2
+    pairs_over = good_desc(heads=1, grid=(91, 256, 256))  # 23296 x 93184 >= 2^31
+    assert native.regen_attn_workspace_size(pairs_over) == 0
+    s, h = native.regen_attn_create(pairs_over)
+    assert s == native.REGEN_ERR_INVALID_ARGUMENT and h is None
+    assert "pairs" in native.regen_attn_last_error()
 
 
 def test_create_rejects_null_desc():

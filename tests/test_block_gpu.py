@@ -94,9 +94,10 @@ def test_linear_window_qkv_shape_sampled_rows():
     assert err.sum() / np.abs(ref).sum() <= 3e-3
 
 
-@pytest.mark.skip(reason="this case (the 10920-token block, formerly with hipBLASLt projections) "
-                         "faulted the GPU and its cause was not shown; it stays off the GPU")
 def test_block_window_sampled_rows():
+    # Every access of this configuration is checked in bounds on the CPU by
+    # tests/test_bounds_cpu.py::test_block_in_bounds (QKV GEMM, rope_k_vt and
+    # attention on the fused projection output, merge, output GEMM).
     w = synth.WORKLOADS["window25_12x128_n10920"]
     say("case attention block, 25-frame window (sampled rows)")
     x, w_qkv, w_o = synth.make_block_inputs(w, 1, 7, device="cuda")
