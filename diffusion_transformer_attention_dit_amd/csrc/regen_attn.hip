@@ -121,6 +121,22 @@ regen_status resolve(const regen_attn_desc* d, Problem* p) {
     return REGEN_OK;
 }
 
+// Rotary geometry of p (axis extents, pairs, table offsets); returns the
+// number of table entries, T P_t + H P_h + W P_w.
+int64_t rope_geometry(const Problem& p, regen::RopeGeom* geo) {
+    geo->T = p.T;
+    geo->H = p.H;
+    geo->W = p.W;
+    const int extent[3] = {p.T, p.H, p.W};
+    int64_t off = 0;
+    for (int a = 0; a < 3; ++a) {
+        geo->pairs[a] = p.pairs[a];
+        geo->off[a] = int(std::min<int64_t>(off, INT32_MAX));
+        off += int64_t(extent[a]) * p.pairs[a];
+    }
+    return off;
+}
+
 size_t workspace_bytes(const Problem& p) {
     // Kr and Vt, bf16 each.
     return size_t(2) * size_t(p.heads) * size_t(p.tokens_pad) * size_t(p.head_dim) * 2;
@@ -134,20 +150,37 @@ struct ProfRecord {
     hipEvent_t ev[4];
 };
 
+// One set of the device buffers a call writes besides its output. A handle
+// holds kSlots of them, so that calls issued on different streams can run at
+// the same time; acquire_slot() picks one per call and fences it with its
+// event, which makes a handle read-only from the caller's point of view.
+struct Slot {
+    uint16_t* kr;        // rotated K, [heads][Npad/64] fragment-ordered tiles
+    uint16_t* vt;        // transposed V, same layout
+    uint16_t* part_o;    // split-tile O / l, bf16 [2P][BM][D]
+    float* part_ml;      // split-tile (m, l)      [2P][BM][2]
+    uint16_t* qkv;       // attention blocks only: projection output [N][3 hidden]
+    uint16_t* attn_out;  // attention blocks only: attention output  [N][hidden]
+    hipEvent_t done;     // recorded after the last kernel of every call using the slot
+    hipStream_t last;    // the stream of that call
+    bool used;
+    uint64_t stamp;      // order of last use
+};
+constexpr int kSlots = 2;
+
 struct regen_attn {
     int device;
+    std::mutex mu;  // guards the slots and the profiling lists
     std::vector<ProfRecord> prof_pending;  // recorded, not yet read
     std::vector<ProfRecord> prof_free;     // created, reusable
     Problem p;
     regen::RopeGeom geo;
     float2* d_tab;     // rotary (cos, sin) per axis
     float2* d_tab_id;  // the same table with every angle 0 (unrotated calls)
-    uint16_t* d_kr;  // workspace: rotated K
-    uint16_t* d_vt;  // workspace: transposed V
-    int P;           // persistent attention workgroups
-    int Pc;          // cross_attn_kernel workgroups (one round of resident slots)
-    uint16_t* d_part_o;  // split-tile O / l, bf16 [2P][BM][D]
-    float* d_part_ml;  // split-tile (m, l)       [2P][BM][2]
+    int P;             // persistent attention workgroups
+    int Pc;            // cross_attn_kernel workgroups (one round of resident slots)
+    Slot slot[kSlots];
+    uint64_t stamp;
 };
 
 namespace {
@@ -162,6 +195,66 @@ regen_status occupancy(int* blocks_per_cu, int* cross_blocks_per_cu) {
     if (e != hipSuccess) return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     if (*blocks_per_cu < 1) *blocks_per_cu = 1;
     if (*cross_blocks_per_cu < 1) *cross_blocks_per_cu = 1;
+    return REGEN_OK;
+}
+
+// Release a handle's device memory and events (each pointer may be NULL) and
+// the handle. Waits first for the last call on each slot.
+void free_handle(regen_attn* h) {
+    int cur = 0;
+    const bool switched = hipGetDevice(&cur) == hipSuccess && cur != h->device &&
+                          hipSetDevice(h->device) == hipSuccess;
+    for (Slot& sl : h->slot)
+        if (sl.done && sl.used) (void)hipEventSynchronize(sl.done);
+    if (h->d_tab) (void)hipFree(h->d_tab);
+    for (Slot& sl : h->slot) {
+        for (void* ptr : {(void*)sl.kr, (void*)sl.vt, (void*)sl.part_o, (void*)sl.part_ml, (void*)sl.qkv,
+                          (void*)sl.attn_out})
+            if (ptr) (void)hipFree(ptr);
+        if (sl.done) (void)hipEventDestroy(sl.done);
+    }
+    for (auto* list : {&h->prof_pending, &h->prof_free})
+        for (ProfRecord& r : *list)
+            for (hipEvent_t ev : r.ev) (void)hipEventDestroy(ev);
+    if (switched) (void)hipSetDevice(cur);
+    delete h;
+}
+
+// The slot for a call on stream st (h->mu held): the one this stream used
+// last (stream order already puts the new call after that one), else one
+// never used, else the least recently used one, after making st wait for
+// the last call that used it.
+regen_status acquire_slot(regen_attn* h, hipStream_t st, Slot** out) {
+    Slot* pick = nullptr;
+    for (Slot& sl : h->slot)
+        if (sl.used && sl.last == st) {
+            pick = &sl;
+            break;
+        }
+    if (!pick)
+        for (Slot& sl : h->slot)
+            if (!sl.used) {
+                pick = &sl;
+                break;
+            }
+    if (!pick) {
+        pick = &h->slot[0];
+        for (Slot& sl : h->slot)
+            if (sl.stamp < pick->stamp) pick = &sl;
+        const hipError_t e = hipStreamWaitEvent(st, pick->done, 0);
+        if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent");
+    }
+    *out = pick;
+    return REGEN_OK;
+}
+
+// After a call's kernels are enqueued on st (h->mu held).
+regen_status release_slot(regen_attn* h, Slot* sl, hipStream_t st) {
+    const hipError_t e = hipEventRecord(sl->done, st);
+    if (e != hipSuccess) return fail_hip(e, "hipEventRecord");
+    sl->last = st;
+    sl->used = true;
+    sl->stamp = ++h->stamp;
     return REGEN_OK;
 }
 
@@ -216,17 +309,11 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
 
     // Rotary tables in fp64, stored as fp32 (cos, sin).
     regen::RopeGeom geo;
-    geo.T = p.T;
-    geo.H = p.H;
-    geo.W = p.W;
+    const int64_t entries = rope_geometry(p, &geo);
+    if (entries >= (int64_t(1) << 31))
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "rotary table too large (grid extent x pairs >= 2^31)");
     const int extent[3] = {p.T, p.H, p.W};
-    int off = 0;
-    for (int a = 0; a < 3; ++a) {
-        geo.pairs[a] = p.pairs[a];
-        geo.off[a] = off;
-        off += extent[a] * p.pairs[a];
-    }
-    std::vector<float2> tab(off);
+    std::vector<float2> tab(entries);
     const bool rope = !(p.flags & REGEN_ATTN_NO_ROPE);
     for (int a = 0; a < 3; ++a)
         for (int pos = 0; pos < extent[a]; ++pos)
@@ -245,9 +332,8 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
     h->p = p;
     h->geo = geo;
     h->d_tab = h->d_tab_id = nullptr;
-    h->d_kr = h->d_vt = nullptr;
-    h->d_part_o = nullptr;
-    h->d_part_ml = nullptr;
+    h->stamp = 0;
+    for (Slot& sl : h->slot) sl = Slot{};
     int per_cu = 1, cross_per_cu = 1;
     s = p.head_dim == 128 ? occupancy<128>(&per_cu, &cross_per_cu) : occupancy<64>(&per_cu, &cross_per_cu);
     if (s != REGEN_OK) {
@@ -260,30 +346,26 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
 
     const size_t tab_bytes = tab.size() * sizeof(float2);
     const size_t half_ws = workspace_bytes(p) / 2;
-    auto cleanup = [&]() {
-        if (h->d_tab) (void)hipFree(h->d_tab);
-        if (h->d_kr) (void)hipFree(h->d_kr);
-        if (h->d_vt) (void)hipFree(h->d_vt);
-        if (h->d_part_o) (void)hipFree(h->d_part_o);
-        if (h->d_part_ml) (void)hipFree(h->d_part_ml);
-        delete h;
-    };
     const size_t part_o_bytes = size_t(2) * h->P * kBM * p.head_dim * sizeof(uint16_t);
     const size_t part_ml_bytes = size_t(2) * h->P * kBM * 2 * sizeof(float);
-    if ((e = hipMalloc(&h->d_tab, 2 * tab_bytes)) != hipSuccess ||
-        (e = hipMalloc(&h->d_kr, half_ws)) != hipSuccess ||
-        (e = hipMalloc(&h->d_vt, half_ws)) != hipSuccess ||
-        (e = hipMalloc(&h->d_part_o, part_o_bytes)) != hipSuccess ||
-        (e = hipMalloc(&h->d_part_ml, part_ml_bytes)) != hipSuccess) {
+    e = hipMalloc(&h->d_tab, 2 * tab_bytes);
+    for (Slot& sl : h->slot) {
+        if (e == hipSuccess) e = hipMalloc(&sl.kr, half_ws);
+        if (e == hipSuccess) e = hipMalloc(&sl.vt, half_ws);
+        if (e == hipSuccess) e = hipMalloc(&sl.part_o, part_o_bytes);
+        if (e == hipSuccess) e = hipMalloc(&sl.part_ml, part_ml_bytes);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&sl.done, hipEventDisableTiming);
+    }
+    if (e != hipSuccess) {
         (void)hipGetLastError();
-        cleanup();
+        free_handle(h);
         return fail(e == hipErrorOutOfMemory ? REGEN_ERR_OUT_OF_MEMORY : REGEN_ERR_HIP,
                     std::string("device allocation failed: ") + hipGetErrorString(e));
     }
     h->d_tab_id = h->d_tab + tab.size();
     tab.resize(2 * tab.size(), float2{1.0f, 0.0f});
     if ((e = hipMemcpy(h->d_tab, tab.data(), 2 * tab_bytes, hipMemcpyHostToDevice)) != hipSuccess) {
-        cleanup();
+        free_handle(h);
         return fail_hip(e, "hipMemcpy of the rotary table");
     }
     {
@@ -308,18 +390,29 @@ struct Strides {
     long long qh, qn, kh, kn, oh, on;
 };
 
-regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, const void* k,
-                     const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse,
-                     void* stream, bool cross, const Strides& sd);
+// What one call's kernels need besides its arguments: the problem, the
+// rotary tables, the workgroup counts and the buffers of one slot.
+struct Ctx {
+    const Problem* p;
+    const regen::RopeGeom* geo;
+    const float2* tab;
+    const float2* tab_id;
+    int P, Pc;
+    uint16_t* kr;
+    uint16_t* vt;
+    uint16_t* part_o;
+    float* part_ml;
+};
 
-// One attention call: query tokens [q_begin, q_begin + nq) against key
-// tokens [kv_begin, kv_begin + nk) of the handle's window.
-regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, const void* k,
-                    const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse,
-                    void* stream, bool cross = false) {
-    if (!h || !is_live(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is NULL or not live");
+regen_status enqueue(const Ctx& c, const void* q, int64_t q_begin, int64_t nq, const void* k,
+                     const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse, void* stream,
+                     bool cross, const Strides& sd, ProfRecord* rec);
+
+// Checks of one call's ranges and pointers against problem p.
+regen_status check_call(const Problem& p, const void* q, int64_t q_begin, int64_t nq, const void* k,
+                        const void* v, int64_t kv_begin, int64_t nk, const void* o, const float* lse,
+                        bool cross) {
     if (!q || !k || !v || !o) return fail(REGEN_ERR_INVALID_ARGUMENT, "q, k, v, o must be non-NULL");
-    const Problem& p = h->p;
     if (q_begin < 0 || nq < 1 || q_begin + nq > p.tokens)
         return fail(REGEN_ERR_INVALID_ARGUMENT, "query range outside [0, grid_t*grid_h*grid_w)");
     if (cross) {
@@ -344,7 +437,11 @@ regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, 
                 overlaps(uintptr_t(lse), lbytes, ptrs[2], kbytes) ||
                 overlaps(uintptr_t(lse), lbytes, ptrs[3], qbytes)))
         return fail(REGEN_ERR_INVALID_ARGUMENT, "lse overlaps q, k, v or o");
+    return REGEN_OK;
+}
 
+// Strides of the caller's q, k, v, o under the problem's layout flag.
+Strides caller_strides(const Problem& p, int64_t nq, int64_t nk) {
     const bool tm = (p.flags & REGEN_ATTN_TOKEN_MAJOR) != 0;
     const long long D = p.head_dim;
     Strides sd;
@@ -352,7 +449,71 @@ regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, 
     sd.qn = sd.on = tm ? p.heads * D : D;
     sd.kh = tm ? D : nk * D;
     sd.kn = tm ? p.heads * D : D;
-    return enqueue(h, q, q_begin, nq, k, v, kv_begin, nk, o, lse, stream, cross, sd);
+    return sd;
+}
+
+Ctx handle_ctx(const regen_attn* h, const Slot* sl) {
+    return Ctx{&h->p, &h->geo, h->d_tab, h->d_tab_id, h->P, h->Pc, sl->kr, sl->vt, sl->part_o,
+               sl->part_ml};
+}
+
+// One profiling record of handle h (h->mu held), or NULL for an unprofiled handle.
+regen_status prof_record(regen_attn* h, ProfRecord** out) {
+    *out = nullptr;
+    if (!(h->p.flags & REGEN_ATTN_PROFILE)) return REGEN_OK;
+    ProfRecord rec{};
+    if (!h->prof_free.empty()) {
+        rec = h->prof_free.back();
+        h->prof_free.pop_back();
+    } else {
+        for (int i = 0; i < 4; ++i) {
+            const hipError_t e = hipEventCreate(&rec.ev[i]);
+            if (e != hipSuccess) {
+                for (int j = 0; j < i; ++j) (void)hipEventDestroy(rec.ev[j]);
+                return fail_hip(e, "hipEventCreate");
+            }
+        }
+    }
+    h->prof_pending.push_back(rec);
+    *out = &h->prof_pending.back();
+    return REGEN_OK;
+}
+
+// Enqueue `body(ctx, rec)` on stream st with one of handle h's slots.
+template <typename F>
+regen_status with_slot(regen_attn* h, void* stream, F body) {
+    int cur = -1;
+    const hipError_t ge = hipGetDevice(&cur);
+    if (ge != hipSuccess) return fail_hip(ge, "hipGetDevice");
+    if (cur != h->device)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "the current HIP device is not the handle's device");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lk(h->mu);
+    Slot* sl = nullptr;
+    regen_status s = acquire_slot(h, st, &sl);
+    if (s != REGEN_OK) return s;
+    ProfRecord* rec = nullptr;
+    s = prof_record(h, &rec);
+    if (s != REGEN_OK) return s;
+    s = body(sl, rec);
+    const regen_status r = release_slot(h, sl, st);
+    return s != REGEN_OK ? s : r;
+}
+
+// One attention call: query tokens [q_begin, q_begin + nq) against key
+// tokens [kv_begin, kv_begin + nk) of the handle's window.
+regen_status launch(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, const void* k,
+                    const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse,
+                    void* stream, bool cross = false) {
+    if (!h || !is_live(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is NULL or not live");
+    const Problem& p = h->p;
+    regen_status s = check_call(p, q, q_begin, nq, k, v, kv_begin, nk, o, lse, cross);
+    if (s != REGEN_OK) return s;
+    const Strides sd = caller_strides(p, nq, nk);
+    return with_slot(h, stream, [&](Slot* sl, ProfRecord* rec) {
+        return enqueue(handle_ctx(h, sl), q, q_begin, nq, k, v, kv_begin, nk, o, lse, stream, cross, sd,
+                       rec);
+    });
 }
 
 // Schedule of the persistent attention kernel over P workgroups for one
@@ -374,17 +535,12 @@ bool make_sched(int heads, int64_t nq, int64_t nk, int P, regen::Sched* sc, int6
     return true;
 }
 
-// Enqueue the kernels of one call whose arguments have been checked.
-regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq, const void* k,
-                     const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse,
-                     void* stream, bool cross, const Strides& sd) {
-    const Problem& p = h->p;
-    int cur = -1;
-    hipError_t ge = hipGetDevice(&cur);
-    if (ge != hipSuccess) return fail_hip(ge, "hipGetDevice");
-    if (cur != h->device)
-        return fail(REGEN_ERR_INVALID_ARGUMENT, "the current HIP device is not the handle's device");
-
+// Enqueue the kernels of one call whose arguments have been checked; with
+// rec, record its events around them.
+regen_status enqueue(const Ctx& c, const void* q, int64_t q_begin, int64_t nq, const void* k,
+                     const void* v, int64_t kv_begin, int64_t nk, void* o, float* lse, void* stream,
+                     bool cross, const Strides& sd, ProfRecord* rec) {
+    const Problem& p = *c.p;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int Nq = int(nq), Nk = int(nk);
     const int Npad = int((nk + regen::kPrepKeys - 1) / regen::kPrepKeys * regen::kPrepKeys);
@@ -393,7 +549,7 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
     dim3 pgrid(unsigned(Npad / regen::kPrepBlock), unsigned(p.heads));
     regen::Sched sc;
     int64_t rem_tiles = 0;
-    if (!make_sched(p.heads, nq, nk, h->P, &sc, &rem_tiles))
+    if (!make_sched(p.heads, nq, nk, c.P, &sc, &rem_tiles))
         return fail(REGEN_ERR_INVALID_ARGUMENT,
                     "too many (query tile, key block) pairs for one call (heads * ceil(q/256) * "
                     "ceil(k/64) must stay below 2^31)");
@@ -406,28 +562,14 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
     uint16_t* o16 = static_cast<uint16_t*>(o);
     const int q_off = int(q_begin), k_off = int(kv_begin);
     // Cross-attention rotates nothing: the identity table.
-    const float2* tab = cross ? h->d_tab_id : h->d_tab;
+    const float2* tab = cross ? c.tab_id : c.tab;
+    const regen::RopeGeom& geo = *c.geo;
     const long long qh = sd.qh, qn = sd.qn, kh = sd.kh, kn = sd.kn, oh = sd.oh, on = sd.on;
 
-    ProfRecord rec{};
-    const bool prof = (p.flags & REGEN_ATTN_PROFILE) != 0;
-    if (prof) {
-        if (!h->prof_free.empty()) {
-            rec = h->prof_free.back();
-            h->prof_free.pop_back();
-        } else {
-            for (int i = 0; i < 4; ++i) {
-                hipError_t ee = hipEventCreate(&rec.ev[i]);
-                if (ee != hipSuccess) {
-                    for (int j = 0; j < i; ++j) (void)hipEventDestroy(rec.ev[j]);
-                    return fail_hip(ee, "hipEventCreate");
-                }
-            }
-        }
-        (void)hipEventRecord(rec.ev[0], st);
-    }
+    const bool prof = rec != nullptr;
+    if (prof) (void)hipEventRecord(rec->ev[0], st);
     auto mark = [&](int i) {
-        if (prof) (void)hipEventRecord(rec.ev[i], st);
+        if (prof) (void)hipEventRecord(rec->ev[i], st);
     };
 
     // A short context stays in LDS: one kernel, one pass over the queries.
@@ -437,7 +579,7 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
     const bool short_ctx = cross && nk <= regen::kCrossMaxKeys && nk * kn * 2 < (int64_t(1) << 31) &&
                            span_q < (int64_t(1) << 31) && nq * 4 < (int64_t(1) << 31);
     const int64_t cross_units = int64_t(p.heads) * ((nq + 31) / 32);
-    const dim3 cgrid{unsigned(std::min<int64_t>(h->Pc, cross_units)), 1u, 1u};
+    const dim3 cgrid{unsigned(std::min<int64_t>(c.Pc, cross_units)), 1u, 1u};
     if (short_ctx) {
         mark(1);
         if (p.head_dim == 128) {
@@ -457,43 +599,40 @@ regen_status enqueue(regen_attn_t h, const void* q, int64_t q_begin, int64_t nq,
         }
         mark(2);
     } else if (p.head_dim == 128) {
-        hipLaunchKernelGGL(regen::rope_k_vt_kernel<128>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
-                           h->d_vt, tab, h->geo, Nk, Npad, k_off, kh, kn);
+        hipLaunchKernelGGL(regen::rope_k_vt_kernel<128>, pgrid, dim3(256), 0, st, k16, v16, c.kr,
+                           c.vt, tab, geo, Nk, Npad, k_off, kh, kn);
         mark(1);
-        hipLaunchKernelGGL((regen::attn_fwd_kernel<128, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
-                           st, q16, h->d_kr, h->d_vt, o16, lse, tab, h->geo, Nq, Nk, Npad,
-                           q_off, qh, qn, oh, on, sc, c2, int(!cross), h->d_part_o, h->d_part_ml);
+        hipLaunchKernelGGL((regen::attn_fwd_kernel<128, kBN, kNW>), dim3(c.P), dim3(kNW * 64), 0,
+                           st, q16, c.kr, c.vt, o16, lse, tab, geo, Nq, Nk, Npad,
+                           q_off, qh, qn, oh, on, sc, c2, int(!cross), c.part_o, c.part_ml);
         mark(2);
         if (rem_tiles > 0) {
             if (mw4)
                 hipLaunchKernelGGL((regen::merge_kernel<128, kNW, 4>), mgrid, dim3(256), 0, st, o16,
-                                   lse, h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
+                                   lse, c.part_o, c.part_ml, Nq, sc, oh, on);
             else
                 hipLaunchKernelGGL((regen::merge_kernel<128, kNW, 1>), mgrid, dim3(256), 0, st, o16,
-                                   lse, h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
+                                   lse, c.part_o, c.part_ml, Nq, sc, oh, on);
         }
     } else {
-        hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, h->d_kr,
-                           h->d_vt, tab, h->geo, Nk, Npad, k_off, kh, kn);
+        hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, c.kr,
+                           c.vt, tab, geo, Nk, Npad, k_off, kh, kn);
         mark(1);
-        hipLaunchKernelGGL((regen::attn_fwd_kernel<64, kBN, kNW>), dim3(h->P), dim3(kNW * 64), 0,
-                           st, q16, h->d_kr, h->d_vt, o16, lse, tab, h->geo, Nq, Nk, Npad,
-                           q_off, qh, qn, oh, on, sc, c2, int(!cross), h->d_part_o, h->d_part_ml);
+        hipLaunchKernelGGL((regen::attn_fwd_kernel<64, kBN, kNW>), dim3(c.P), dim3(kNW * 64), 0,
+                           st, q16, c.kr, c.vt, o16, lse, tab, geo, Nq, Nk, Npad,
+                           q_off, qh, qn, oh, on, sc, c2, int(!cross), c.part_o, c.part_ml);
         mark(2);
         if (rem_tiles > 0) {
             if (mw4)
                 hipLaunchKernelGGL((regen::merge_kernel<64, kNW, 4>), mgrid, dim3(256), 0, st, o16,
-                                   lse, h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
+                                   lse, c.part_o, c.part_ml, Nq, sc, oh, on);
             else
                 hipLaunchKernelGGL((regen::merge_kernel<64, kNW, 1>), mgrid, dim3(256), 0, st, o16,
-                                   lse, h->d_part_o, h->d_part_ml, Nq, sc, oh, on);
+                                   lse, c.part_o, c.part_ml, Nq, sc, oh, on);
         }
     }
     hipError_t e = hipGetLastError();
-    if (prof) {
-        (void)hipEventRecord(rec.ev[3], st);
-        h->prof_pending.push_back(rec);
-    }
+    if (prof) (void)hipEventRecord(rec->ev[3], st);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     return REGEN_OK;
 }
@@ -651,6 +790,7 @@ regen_status regen_attn_profile_read(regen_attn_t h, double* prep_ms, double* at
     double tp = 0.0, ta = 0.0, tm = 0.0;
     int64_t n = 0;
     regen_status st = REGEN_OK;
+    std::lock_guard<std::mutex> lk(h->mu);
     for (ProfRecord& r : h->prof_pending) {
         float a = 0.0f, b = 0.0f, c = 0.0f;
         hipError_t e = hipEventSynchronize(r.ev[3]);
@@ -679,19 +819,7 @@ regen_status regen_attn_destroy(regen_attn_t h) {
         std::lock_guard<std::mutex> lk(g_live_mu);
         if (!g_live.erase(h)) return fail(REGEN_ERR_INVALID_ARGUMENT, "handle is not live");
     }
-    int cur = 0;
-    const bool switched = hipGetDevice(&cur) == hipSuccess && cur != h->device &&
-                          hipSetDevice(h->device) == hipSuccess;
-    (void)hipFree(h->d_tab);
-    (void)hipFree(h->d_kr);
-    (void)hipFree(h->d_vt);
-    (void)hipFree(h->d_part_o);
-    (void)hipFree(h->d_part_ml);
-    for (auto* list : {&h->prof_pending, &h->prof_free})
-        for (ProfRecord& r : *list)
-            for (hipEvent_t ev : r.ev) (void)hipEventDestroy(ev);
-    if (switched) (void)hipSetDevice(cur);
-    delete h;
+    free_handle(h);
     return REGEN_OK;
 }
 
@@ -705,10 +833,9 @@ regen_status regen_attn_destroy(regen_attn_t h) {
 // output token-major, so nothing is copied between the three steps.
 // ---------------------------------------------------------------------------
 struct regen_block {
-    regen_attn* attn;    // attention of the block (internal handle)
+    regen_attn* attn;  // attention of the block (internal handle); its slots also
+                       // hold the projection output and the attention output
     int N, hidden;
-    uint16_t* qkv;       // [N][3 hidden]
-    uint16_t* attn_out;  // [N][hidden]
 };
 
 namespace {
@@ -723,8 +850,6 @@ bool block_live(const void* b) {
 
 void block_free(regen_block* b) {
     if (!b) return;
-    if (b->qkv) (void)hipFree(b->qkv);
-    if (b->attn_out) (void)hipFree(b->attn_out);
     if (b->attn) (void)regen_attn_destroy(b->attn);
     delete b;
 }
@@ -847,9 +972,12 @@ regen_status regen_block_create(const regen_attn_desc* desc, regen_block_t* out)
     b->N = int(p.tokens);
     b->hidden = p.heads * p.head_dim;
     const size_t H = size_t(b->hidden), N = size_t(b->N);
-    hipError_t e;
-    if ((e = hipMalloc(&b->qkv, N * 3 * H * 2)) != hipSuccess ||
-        (e = hipMalloc(&b->attn_out, N * H * 2)) != hipSuccess) {
+    hipError_t e = hipSuccess;
+    for (Slot& sl : b->attn->slot) {
+        if (e == hipSuccess) e = hipMalloc(&sl.qkv, N * 3 * H * 2);
+        if (e == hipSuccess) e = hipMalloc(&sl.attn_out, N * H * 2);
+    }
+    if (e != hipSuccess) {
         (void)hipGetLastError();
         block_free(b);
         return fail(e == hipErrorOutOfMemory ? REGEN_ERR_OUT_OF_MEMORY : REGEN_ERR_HIP,
@@ -877,23 +1005,21 @@ regen_status regen_block_forward(regen_block_t b, const void* x, const void* w_q
     if (overlaps(ptrs[3], xb, ptrs[0], xb) || overlaps(ptrs[3], xb, ptrs[1], wqb) ||
         overlaps(ptrs[3], xb, ptrs[2], wob))
         return fail(REGEN_ERR_INVALID_ARGUMENT, "y overlaps x, w_qkv or w_o");
-    int cur = -1;
-    hipError_t ge = hipGetDevice(&cur);
-    if (ge != hipSuccess) return fail_hip(ge, "hipGetDevice");
-    if (cur != b->attn->device)
-        return fail(REGEN_ERR_INVALID_ARGUMENT, "the current HIP device is not the block's device");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int Hd = b->hidden;
-    regen_status s = gemm(static_cast<const uint16_t*>(x), Hd, static_cast<const uint16_t*>(w_qkv), Hd,
-                          b->qkv, 3 * Hd, b->N, 3 * Hd, Hd, st);
-    if (s != REGEN_OK) return s;
-    const long long D = b->attn->p.head_dim;
-    const Strides sd{D, 3LL * Hd, D, 3LL * Hd, D, Hd};
-    s = enqueue(b->attn, b->qkv, 0, b->N, b->qkv + Hd, b->qkv + 2 * Hd, 0, b->N,
-                             b->attn_out, nullptr, stream, false, sd);
-    if (s != REGEN_OK) return s;
-    return gemm(b->attn_out, Hd, static_cast<const uint16_t*>(w_o), Hd, static_cast<uint16_t*>(y), Hd,
-                b->N, Hd, Hd, st);
+    regen_attn* h = b->attn;
+    return with_slot(h, stream, [&](Slot* sl, ProfRecord* rec) {
+        regen_status s = gemm(static_cast<const uint16_t*>(x), Hd, static_cast<const uint16_t*>(w_qkv), Hd,
+                              sl->qkv, 3 * Hd, b->N, 3 * Hd, Hd, st);
+        if (s != REGEN_OK) return s;
+        const long long D = h->p.head_dim;
+        const Strides sd{D, 3LL * Hd, D, 3LL * Hd, D, Hd};
+        s = enqueue(handle_ctx(h, sl), sl->qkv, 0, b->N, sl->qkv + Hd, sl->qkv + 2 * Hd, 0, b->N,
+                    sl->attn_out, nullptr, stream, false, sd, rec);
+        if (s != REGEN_OK) return s;
+        return gemm(sl->attn_out, Hd, static_cast<const uint16_t*>(w_o), Hd, static_cast<uint16_t*>(y), Hd,
+                    b->N, Hd, Hd, st);
+    });
 }
 
 regen_status regen_block_destroy(regen_block_t b) {

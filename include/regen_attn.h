@@ -35,9 +35,19 @@
  * regen_ulysses_pack).
  *
  * Threading: a handle is bound to the HIP device that was current at
- * create. It owns a device workspace (rotated K and a transposed V), so calls
- * of regen_attn_forward on ONE handle must be ordered: issue them on one
- * stream, or synchronize between streams. Distinct handles are independent.
+ * create, and is read-only for the caller after create: calls on one handle
+ * may be issued from any host thread, on any streams, with no ordering
+ * between them. The handle owns two sets of the device buffers a call writes
+ * besides its output (rotated K, transposed V, split-tile partials, and for
+ * an attention block its projection outputs). A call takes the set its
+ * stream used last, else an unused one, else the least recently used one,
+ * after making its stream wait (hipStreamWaitEvent) for the last call that
+ * used that set; after enqueueing, it records the set's event on its stream.
+ * So calls on two streams run at the same time, and a third stream is
+ * ordered behind one of them. A stream handle must not be destroyed and
+ * re-created at the same address while calls on it are in flight (the
+ * library tells streams apart by their handle value). Distinct handles are
+ * independent.
  */
 #ifndef REGEN_ATTN_H
 #define REGEN_ATTN_H
@@ -99,20 +109,20 @@ typedef struct regen_attn *regen_attn_t;
 /*
  * Create a handle for one problem shape on the current HIP device.
  * Allocates the handle, the per-axis rotary tables (fp64 on the host,
- * stored as fp32 cos/sin), a device workspace of
- * 2 * heads * ceil(tokens/128)*128 * head_dim * 2 bytes (rotated K and
- * transposed V; see regen_attn_workspace_size) and a scratch area for query
- * tiles whose keys are split over several workgroups of the persistent
- * attention kernel: 2 * P * 256 * (2 * head_dim + 8) bytes (bf16 O/l and
- * fp32 (m, l) per row), P = resident workgroups of the device (one per
- * compute unit on MI355X: 33 MiB at
- * head_dim 128).
+ * stored as fp32 cos/sin) and two sets (see Threading above) of: a device
+ * workspace of 2 * heads * ceil(tokens/128)*128 * head_dim * 2 bytes
+ * (rotated K and transposed V; see regen_attn_workspace_size) and a scratch
+ * area for query tiles whose keys are split over several workgroups of the
+ * persistent attention kernel: 2 * P * 256 * (2 * head_dim + 8) bytes (bf16
+ * O/l and fp32 (m, l) per row), P = resident workgroups of the device (one
+ * per compute unit on MI355X: 33 MiB at head_dim 128).
  * On success *out receives the handle; on any failure *out is set to NULL
  * (when out is not NULL) and the status says why:
  *   INVALID_ARGUMENT (NULL desc/out, wrong struct_size, heads/grid < 1,
  *   bad pairs split, base or scale < 0, unknown flags, tokens > 2^30, one
  *   head's rotated K reaching 2^31 bytes: ceil(tokens/128)*128 * head_dim *
- *   2 >= 2^31),
+ *   2 >= 2^31, or heads * ceil(tokens/256) * ceil(tokens/64) >= 2^31: the
+ *   attention schedule numbers its (query tile, key block) pairs in 31 bits),
  *   UNSUPPORTED (head_dim not 64/128, current device is not gfx950),
  *   NO_DEVICE, OUT_OF_MEMORY, HIP.
  */
@@ -149,8 +159,7 @@ regen_status regen_attn_forward(regen_attn_t h, const void *q, const void *k,
  * in the file comment). Ranges must satisfy 0 <= begin, 1 <= count,
  * begin + count <= grid_t*grid_h*grid_w. Pointers: device memory, o 16-byte
  * aligned and not overlapping q, k, v; lse 4-byte aligned and not
- * overlapping any other buffer. The same ordering rule as regen_attn_forward
- * applies (the handle's workspace is reused). regen_attn_forward(h, q, k, v,
+ * overlapping any other buffer. regen_attn_forward(h, q, k, v,
  * o, s) equals this call with both ranges covering the window and lse NULL.
  * Errors: INVALID_ARGUMENT (bad handle, range, pointer, alignment or
  * overlap), HIP (launch failure).
@@ -171,8 +180,7 @@ regen_status regen_attn_forward_range(regen_attn_t h, const void *q, int64_t q_b
  *            [head_dim] with REGEN_ATTN_TOKEN_MAJOR)
  *   o      : like q;  lse : [heads][tokens] fp32 or NULL
  * 1 <= ctx_len <= grid_t*grid_h*grid_w (the workspace is sized by the
- * window). Same pointer rules, ordering rule and errors as
- * regen_attn_forward_range. A context of at most 256 tokens is held whole in
+ * window). Same pointer rules and errors as regen_attn_forward_range. A context of at most 256 tokens is held whole in
  * on-chip memory by one kernel that reads k_ctx and v_ctx directly (the
  * handle's workspace is not touched); longer ones go through the workspace
  * like regen_attn_forward.
@@ -259,10 +267,11 @@ regen_status regen_linear(const void *x, const void *w, void *y, int64_t rows, i
  * applies the rotation while loading. All pointers are device memory,
  * 16-byte aligned, owned by the caller. regen_block_create takes the same
  * description as regen_attn_create (without REGEN_ATTN_TOKEN_MAJOR or
- * REGEN_ATTN_PROFILE) and allocates the attention workspace, the projection
- * output (tokens * 3 hidden bf16) and the attention output (tokens * hidden
- * bf16); calls on one block must be ordered like calls on one attention
- * handle. Errors as for the attention calls.
+ * REGEN_ATTN_PROFILE) and allocates two sets of the attention workspace,
+ * the projection output (tokens * 3 hidden bf16) and the attention output
+ * (tokens * hidden bf16); like an attention handle, a block is read-only
+ * after create and may be used from several streams and threads at once.
+ * Errors as for the attention calls.
  */
 typedef struct regen_block *regen_block_t;
 regen_status regen_block_create(const regen_attn_desc *desc, regen_block_t *out);
@@ -271,8 +280,9 @@ regen_status regen_block_forward(regen_block_t b, const void *x, const void *w_q
 regen_status regen_block_destroy(regen_block_t b);
 
 /*
- * Free the handle, its tables and workspace. No call on the handle may still
- * be in flight (the device memory is released immediately). NULL is a no-op
+ * Free the handle, its tables and workspace, after waiting for the last
+ * call on each of its buffer sets. No call on the handle may be issued
+ * during or after destroy. NULL is a no-op
  * returning REGEN_OK; a handle that is not live gives INVALID_ARGUMENT.
  */
 regen_status regen_attn_destroy(regen_attn_t h);
