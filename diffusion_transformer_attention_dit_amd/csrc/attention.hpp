@@ -64,6 +64,21 @@ __device__ __forceinline__ float2 rope_cs(const float2* __restrict__ tab, const 
     return tab[idx];
 }
 
+// rope_table_kernel: the (cos, sin) table of geometry g, computed on the
+// device in fp64 and stored as fp32: entry off[a] + pos * pairs[a] + j holds
+// the angle pos * base^(-j / pairs[a]) of pair j of axis a (every angle 0
+// when rope == 0). Grid ceil(entries / 256), 256 threads.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, RopeGeom g, double base,
+                                                        int rope, int entries) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= entries) return;
+    const int a = i < g.off[1] ? 0 : (i < g.off[2] ? 1 : 2);
+    const int r = i - g.off[a], pos = r / g.pairs[a], j = r % g.pairs[a];
+    const double theta = pow(base, -double(j) / double(g.pairs[a]));
+    const double phi = double(pos) * theta;
+    tab[i] = rope ? make_float2(float(cos(phi)), float(sin(phi))) : make_float2(1.0f, 0.0f);
+}
+
 // Rotate the 4 pairs held in one 16-byte chunk (8 bf16, pairs i0..i0+3),
 // scale by `mul` and round to bf16.
 __device__ __forceinline__ uint4 rope_chunk(uint4 in, const float2* __restrict__ tab,

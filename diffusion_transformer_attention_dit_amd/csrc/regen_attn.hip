@@ -1034,3 +1034,113 @@ regen_status regen_block_destroy(regen_block_t b) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The allocation-free forward (regen_attn_forward_noalloc): the kernels of
+// regen_attn_forward, with the rotary table, the rotated K / transposed V and
+// the split-tile partials in one file-scope device array. Its device address
+// is looked up once per device (hipGetSymbolAddress) and only that address is
+// handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[REGEN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+struct StaticDevice {
+    unsigned char* ptr;  // device address of `scratch` on this device
+    int slots[2];        // resident attention workgroups, head_dim 64 / 128
+    int cross_slots[2];  // resident cross_attn_kernel workgroups, head_dim 64 / 128
+    bool ready;
+};
+std::mutex g_static_mu;
+StaticDevice g_static[kMaxDevices];
+
+// Per-device set-up on first use, with the device current: the architecture
+// check, the scratch array's device address, the resident workgroup counts.
+regen_status static_device(int dev, StaticDevice* out) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(REGEN_ERR_UNSUPPORTED, "device index above 63");
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    StaticDevice& sd = g_static[dev];
+    if (!sd.ready) {
+        hipDeviceProp_t prop;
+        hipError_t e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail_hip(e, "hipGetDeviceProperties");
+        if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+            return fail(REGEN_ERR_UNSUPPORTED,
+                        std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950");
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress of the static scratch");
+        if (!ptr) return fail(REGEN_ERR_HIP, "hipGetSymbolAddress returned no address for the static scratch");
+        int a64 = 1, c64 = 1, a128 = 1, c128 = 1;
+        regen_status s = occupancy<64>(&a64, &c64);
+        if (s == REGEN_OK) s = occupancy<128>(&a128, &c128);
+        if (s != REGEN_OK) return s;
+        const int cus = prop.multiProcessorCount;
+        sd.ptr = static_cast<unsigned char*>(ptr);
+        sd.slots[0] = a64 * cus;
+        sd.slots[1] = a128 * cus;
+        sd.cross_slots[0] = c64 * cus;
+        sd.cross_slots[1] = c128 * cus;
+        sd.ready = true;
+    }
+    *out = sd;
+    return REGEN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+regen_status regen_attn_forward_noalloc(const regen_attn_desc* desc, const void* q, const void* k,
+                                        const void* v, void* o, void* stream) {
+    g_last_error.clear();
+    Problem p;
+    regen_status s = resolve(desc, &p);
+    if (s != REGEN_OK) return s;
+    if (p.flags & REGEN_ATTN_PROFILE)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "the allocation-free forward takes no profiling flag");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    StaticDevice sd{};
+    s = static_device(dev, &sd);
+    if (s != REGEN_OK) return s;
+    const int hsel = p.head_dim == 128 ? 1 : 0;
+
+    regen::RopeGeom geo;
+    const int64_t entries = rope_geometry(p, &geo);
+    const int P = int(std::min<int64_t>(sd.slots[hsel], p.units));
+    // Scratch layout: table | Kr | Vt | partial O / l | partial (m, l), each
+    // at a 256-byte boundary.
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t tab_b = up(size_t(entries) * sizeof(float2));
+    const size_t half_ws = up(workspace_bytes(p) / 2);
+    const size_t po_b = up(size_t(2) * P * kBM * p.head_dim * sizeof(uint16_t));
+    const size_t pm_b = up(size_t(2) * P * kBM * 2 * sizeof(float));
+    const size_t need = tab_b + 2 * half_ws + po_b + pm_b;
+    if (entries >= (int64_t(1) << 31) || need > REGEN_NOALLOC_SCRATCH_BYTES)
+        return fail(REGEN_ERR_UNSUPPORTED,
+                    "problem needs " + std::to_string(need) + " bytes of scratch; the allocation-free "
+                    "forward holds " + std::to_string(size_t(REGEN_NOALLOC_SCRATCH_BYTES)) +
+                    " (use regen_attn_create / regen_attn_forward)");
+    s = check_call(p, q, 0, p.tokens, k, v, 0, p.tokens, o, nullptr, false);
+    if (s != REGEN_OK) return s;
+    unsigned char* base = sd.ptr;
+    float2* tab = reinterpret_cast<float2*>(base);
+    Ctx c{&p, &geo, tab, tab, P, sd.cross_slots[hsel],
+          reinterpret_cast<uint16_t*>(base + tab_b),
+          reinterpret_cast<uint16_t*>(base + tab_b + half_ws),
+          reinterpret_cast<uint16_t*>(base + tab_b + 2 * half_ws),
+          reinterpret_cast<float*>(base + tab_b + 2 * half_ws + po_b)};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(regen::rope_table_kernel, dim3(unsigned((entries + 255) / 256)), dim3(256), 0, st, tab,
+                       geo, p.base, int(!(p.flags & REGEN_ATTN_NO_ROPE)), int(entries));
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip(e, "rope_table_kernel launch");
+    return enqueue(c, q, 0, p.tokens, k, v, 0, p.tokens, o, nullptr, stream, false,
+                   caller_strides(p, p.tokens, p.tokens), nullptr);
+}
+
+}  // extern "C"

@@ -38,7 +38,11 @@ EXPORTS = (
     "regen_attn_last_error",
     "regen_attn_workspace_size",
     "regen_attn_profile_read",
+    "regen_attn_forward_noalloc",
 )
+
+# Size of the static device scratch behind regen_attn_forward_noalloc.
+REGEN_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 
 class regen_attn_desc(ctypes.Structure):
@@ -119,6 +123,8 @@ def lib():
                                           ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64)]
     L.regen_attn_profile_read.restype = ctypes.c_int
+    L.regen_attn_forward_noalloc.argtypes = [ctypes.POINTER(regen_attn_desc), vp, vp, vp, vp, vp]
+    L.regen_attn_forward_noalloc.restype = ctypes.c_int
     _LIB = L
     return L
 
@@ -142,6 +148,13 @@ def regen_attn_create(desc):
 def regen_attn_forward(handle, q, k, v, o, stream):
     """q, k, v, o, stream are integer device addresses / a hipStream_t value."""
     return lib().regen_attn_forward(handle, q, k, v, o, stream)
+
+
+def regen_attn_forward_noalloc(desc, q, k, v, o, stream):
+    """Handle-free, allocation-free forward; q, k, v, o, stream are integer
+    device addresses / a hipStream_t value."""
+    return lib().regen_attn_forward_noalloc(ctypes.byref(desc) if desc is not None else None, q, k, v, o,
+                                            stream)
 
 
 def regen_attn_forward_range(handle, q, q_begin, q_count, k, v, kv_begin, kv_count, o, lse,

@@ -287,6 +287,31 @@ regen_status regen_block_destroy(regen_block_t b);
  */
 regen_status regen_attn_destroy(regen_attn_t h);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as regen_attn_create + regen_attn_forward + regen_attn_destroy
+ * with the same q, k, v, o arguments and rules, but with no handle and no
+ * allocation. The rotary table (built on the device by a kernel), the rotated
+ * K / transposed V and the split-tile partials live in one static device
+ * array of REGEN_NOALLOC_SCRATCH_BYTES (128 MiB) that the library holds on
+ * each device it runs on until the process ends; the first call on a device
+ * looks its address up. Problems that need more than that (the table, 2 *
+ * heads * ceil(tokens/128)*128 * head_dim * 2 bytes of workspace and
+ * 2 * P * 256 * (2 * head_dim + 8) bytes of partials, P = resident
+ * workgroups) are rejected with UNSUPPORTED: the 25-frame window (12 x 10920
+ * x 128, about 102 MB) fits, the 77-frame clip (12 x 31200 x 128) does not.
+ * Every call on a device shares its one array, and each call leaves its
+ * contents behind: calls that overlap in time on one device (different
+ * streams, or host threads without ordering) race and give wrong results,
+ * so order them. No buffer needs clearing between calls (each call writes
+ * everything it reads). REGEN_ATTN_PROFILE is rejected. Errors as for
+ * regen_attn_create and regen_attn_forward, plus UNSUPPORTED for the size.
+ */
+#define REGEN_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+regen_status regen_attn_forward_noalloc(const regen_attn_desc *desc, const void *q, const void *k,
+                                        const void *v, void *o, void *stream);
+
 /* Static, human-readable name of a status code. Never NULL; do not free. */
 const char *regen_attn_status_string(regen_status s);
 
