@@ -48,9 +48,17 @@ def parse():
     ap.add_argument("--block-only", action="store_true",
                     help="run only the attention-block leg and print it")
     ap.add_argument("--no-clip", action="store_true",
-                    help="skip the 77-frame clip leg (profiling runs of the window alone)")
+                    help="skip the 77-frame clip window leg (profiling runs of the window alone)")
     ap.add_argument("--clip-only", action="store_true",
-                    help="run only the 77-frame clip leg and print it")
+                    help="run only the 77-frame clip window leg and print it")
+    ap.add_argument("--no-block-window", action="store_true",
+                    help="skip the window of attention blocks (profiling runs of the window alone)")
+    ap.add_argument("--block-window-only", action="store_true",
+                    help="run only the window of attention blocks and print it")
+    ap.add_argument("--summarize-rocprof", metavar="DIR", default=None,
+                    help="write the profile summaries of the rocprofv3 passes under DIR (see "
+                         "summarize_rocprof) into --summary-out and exit; needs no GPU")
+    ap.add_argument("--summary-out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run 3 device-to-device copies of this many MiB (to scale HBM "
                          "byte counters against a copy of known size) and exit")
@@ -75,15 +83,10 @@ def counted_traffic(w, algorithmic_bytes):
     passes (FETCH_SIZE, WRITE_SIZE, scaled against a copy of known size), or
     None when the attention kernels' source (common.hpp + attention.hpp) or
     the build flags (build.py) have changed since they were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "attn_fwd_%s_traffic.json" % w.name)
-    csrc = os.path.join(ROOT, "diffusion_transformer_attention_dit_amd", "csrc")
     try:
         doc = json.load(open(path))
-        h = hashlib.sha256()
-        for name in ("csrc/common.hpp", "csrc/attention.hpp", "build.py"):
-            h.update(open(os.path.join(csrc, "..", name), "rb").read())
-        sha = h.hexdigest()
+        sha = kernel_source_sha256()
     except (OSError, ValueError):
         return None
     if doc.get("kernel_source_sha256") != sha:
@@ -291,43 +294,6 @@ def cross_leg(w, reps=20):
     return out
 
 
-def clip_leg(reps=6, sets=2):
-    """The 77-frame clip window's attention (12 heads x 31200 tokens x 128, per-head scale
-    U(0.25, 1)): per-call time of the same library calls over `sets` seeded input sets, with the
-    attention kernel's own duration from the library's kernel events; the window time is 120 x
-    the per-call time (extrapolated, labelled so)."""
-    import torch
-
-    from diffusion_transformer_attention_dit_amd import native, synth
-    c = synth.WORKLOADS["clip77_12x128_n31200"]
-    stream = torch.cuda.current_stream()
-    inputs = [synth.make_qkv(c, 0, b, device="cuda") for b in range(sets)]
-    o = torch.empty_like(inputs[0][0])
-    attn = native.Attention(c.heads, c.head_dim, c.grid, flags=native.REGEN_ATTN_PROFILE)
-    attn.forward(*inputs[0], out=o, stream=stream)
-    torch.cuda.synchronize()
-    attn.profile_read()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for r in range(reps):
-        attn.forward(*inputs[r % sets], out=o, stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    t_call = a.elapsed_time(b) / reps * 1e-3
-    prep_ms, attn_ms, merge_ms, n = attn.profile_read()
-    attn.close()
-    t_attn = attn_ms / n * 1e-3
-    return {"workload": c.name, "calls_timed": reps,
-            "ms_per_call": round(t_call * 1e3, 3),
-            "tflops_per_call": round(c.flops_per_call / t_call / 1e12, 2),
-            "ms_per_window_extrapolated": round(t_call * 1e3 * c.calls, 1),
-            "attention_kernel": {"kernel": "attn_fwd_kernel", "avg_launch_us": round(t_attn * 1e6, 1),
-                                 "bound": "mfma", "achieved": round(c.flops_per_call / t_attn / 1e12, 2),
-                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                 "frac": round(c.flops_per_call / t_attn / 1e12 / PEAK_BF16_TFLOPS, 4)},
-            "prep_us": round(prep_ms / n * 1e3, 1), "merge_us": round(merge_ms / n * 1e3, 1)}
-
-
 def ulysses_leg(w, groups=4, reps=20):
     """One device's share of Ulysses degree 4 at the window's shape: pack its
     token shard of Q for the all-to-all, attention of its head group on the
@@ -385,6 +351,326 @@ def ulysses_leg(w, groups=4, reps=20):
     }
 
 
+def clock_leg(stream):
+    """GPU core clock under a pure bf16 MFMA load (regen_clock_probe), and
+    that load's TFLOP/s: the clock the chip settles at on this machine."""
+    from diffusion_transformer_attention_dit_amd import native
+    ghz, tflops, secs = native.clock_probe(stream=stream)
+    return {"gpu_clock_ghz": round(ghz, 4), "mfma_probe_tflops": round(tflops, 1),
+            "probe_ms": round(secs * 1e3, 2)}
+
+
+def block_window_leg(w, reps=2):
+    """A whole decode window of attention blocks at the window's size:
+    4 steps x 30 blocks, each QKV projection (N x 1536 -> 4608), 3D-RoPE
+    attention and output projection, per-block weights and per-call hidden
+    states resident in HBM before timing."""
+    import torch
+
+    from diffusion_transformer_attention_dit_amd.sampler import BlockWindowDriver
+    stream = torch.cuda.current_stream()
+    print("bench: drawing the block window's inputs", file=sys.stderr, flush=True)
+    drv = BlockWindowDriver(w, device="cuda")
+    drv.run_window(stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        drv.run_window(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / reps * 1e-3
+    out = {"what": "%d self-attention blocks (%d steps x %d blocks) at %d tokens x %d hidden: "
+                   "QKV projection, 3D-RoPE attention, output projection, bf16, random-init weights"
+                   % (drv.calls, drv.steps, drv.blocks, w.tokens, w.heads * w.head_dim),
+           "windows_timed": reps, "ms_per_window": round(t * 1e3, 3),
+           "ms_per_block": round(t * 1e3 / drv.calls, 4),
+           "tflops": round(drv.flops / t / 1e12, 2),
+           "pct_peak": round(100 * drv.flops / t / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "gflop_per_window": round(drv.flops / 1e9, 1)}
+    drv.close()
+    del drv
+    torch.cuda.empty_cache()
+    return out
+
+
+def clip_window_leg(reps=1):
+    """The 77-frame clip window (12 heads x 31200 tokens x 128, per-head scale
+    U(0.25, 1)): 120 calls with fresh seeded inputs (34.5 GB, resident in HBM)
+    timed end to end in one event pair per window; the attention kernel's own
+    duration from the library's kernel events over one more window."""
+    import torch
+
+    from diffusion_transformer_attention_dit_amd import native, synth
+    from diffusion_transformer_attention_dit_amd.sampler import WindowDriver
+    c = synth.WORKLOADS["clip77_12x128_n31200"]
+    stream = torch.cuda.current_stream()
+    print("bench: drawing %d calls of %s" % (c.calls, c.name), file=sys.stderr, flush=True)
+    drv = WindowDriver(c, device="cuda")
+    for (q, k, v) in drv.inputs[:2]:
+        drv.attn.forward(q, k, v, out=drv.outs[0], stream=stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        drv.run_window(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / reps * 1e-3
+    prof = native.Attention(c.heads, c.head_dim, c.grid, flags=native.REGEN_ATTN_PROFILE)
+    for i, (q, k, v) in enumerate(drv.inputs):
+        prof.forward(q, k, v, out=drv.outs[i & 1], stream=stream)
+    prep_ms, attn_ms, merge_ms, n = prof.profile_read()
+    prof.close()
+    drv.close()
+    del drv
+    torch.cuda.empty_cache()
+    t_attn = attn_ms / n * 1e-3
+    return {"workload": c.name, "windows_timed": reps, "calls_per_window": c.calls,
+            "ms_per_window": round(t * 1e3, 2),
+            "tflops": round(c.flops_per_call * c.calls / t / 1e12, 2),
+            "pct_peak": round(100 * c.flops_per_call * c.calls / t / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "attention_kernel": {"kernel": "attn_fwd_kernel", "avg_launch_us": round(t_attn * 1e6, 1),
+                                 "bound": "mfma", "achieved": round(c.flops_per_call / t_attn / 1e12, 2),
+                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(c.flops_per_call / t_attn / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "prep_us": round(prep_ms / n * 1e3, 1), "merge_us": round(merge_ms / n * 1e3, 1)}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (--summarize-rocprof DIR): turns the CSV output of the
+# profiling passes under DIR into the markdown tables and the traffic record
+# kept in profiles/. Expected passes (subdirectories, each a rocprofv3 -d
+# target with -o run --output-format csv): trace (--kernel-trace --stats of
+# the window bench; its stdout JSON line in trace/bench.json), fetch / write
+# (--pmc FETCH_SIZE / WRITE_SIZE of one window), calf / calw (the same
+# counters over --copy-calibration-mib 512), sq1, sq2 (instruction and cycle
+# counters of one window); commands.txt holds the commands, one per line.
+# Any other subdirectory with a kernel trace gets a duration table.
+# ---------------------------------------------------------------------------
+
+def _kernel_short(name):
+    n = name.strip().strip('"')
+    if n.startswith("void "):
+        n = n[5:]
+    depth, out = 0, []
+    for ch in n:  # cut the parameter list (the first '(' outside template brackets)
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            break
+        out.append(ch)
+    return "".join(out).replace("regen::", "").strip()
+
+
+def _find(dirpath, suffix):
+    hits = []
+    for root, _, files in os.walk(dirpath):
+        hits += [os.path.join(root, f) for f in files if f.endswith(suffix)]
+    return sorted(hits)
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _stats(pass_dir):
+    """{kernel: (calls, avg_us, min_us, max_us, pct)} from *_kernel_stats.csv."""
+    out = {}
+    for f in _find(pass_dir, "_kernel_stats.csv"):
+        for r in _read_csv(f):
+            out[_kernel_short(r["Name"])] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                                             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                                             float(r["Percentage"]))
+    return out
+
+
+def _counters(pass_dir):
+    """{kernel: {counter: mean per dispatch}} and {kernel: mean dispatch us}."""
+    acc, dur = {}, {}
+    for f in _find(pass_dir, "_counter_collection.csv"):
+        for r in _read_csv(f):
+            k = _kernel_short(r["Kernel_Name"])
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            dur.setdefault(k, {})[r["Dispatch_Id"]] = d
+    mean = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+    return mean, {k: sum(v.values()) / len(v) for k, v in dur.items()}
+
+
+def _pick(d, prefix):
+    for k in d:
+        if k.startswith(prefix):
+            return k
+    return None
+
+
+def kernel_source_sha256():
+    """Hash of the attention kernels' source and the build flags: the traffic
+    record applies only to the build it was measured on."""
+    import hashlib
+    csrc = os.path.join(ROOT, "diffusion_transformer_attention_dit_amd")
+    h = hashlib.sha256()
+    for name in ("csrc/common.hpp", "csrc/attention.hpp", "build.py"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+def summarize_rocprof(run_dir, out_dir, workload="window25_12x128_n10920"):
+    from diffusion_transformer_attention_dit_amd import synth
+    w = synth.WORKLOADS[workload]
+    os.makedirs(out_dir, exist_ok=True)
+    cmds = []
+    cpath = os.path.join(run_dir, "commands.txt")
+    if os.path.exists(cpath):
+        cmds = [c.rstrip("\n") for c in open(cpath) if c.strip()]
+    L = ["# Kernel profile: 3D-RoPE attention, %s (%d heads x %d tokens x head_dim %d, bf16)"
+         % (w.name, w.heads, w.tokens, w.head_dim), "",
+         "Measured on one MI355X (gfx950) with rocprofv3, each pass its own run of the committed "
+         "bench.py, all in one GPU session; this file and the traffic record beside it were written by "
+         "`python bench.py --summarize-rocprof <dir>` from the passes' CSV output. Commands (run from "
+         "/tmp with TMPDIR=/tmp; $REPO is the repository root):", ""]
+    L += ["    " + c for c in cmds] + [""]
+    trace = _stats(os.path.join(run_dir, "trace"))
+    bench = None
+    bpath = os.path.join(run_dir, "trace", "bench.json")
+    if os.path.exists(bpath):
+        for line in open(bpath):
+            line = line.strip()
+            if line.startswith("{") and '"metric"' in line:
+                bench = json.loads(line)
+    attn = _pick(trace, "attn_fwd_kernel")
+    L += ["## Kernel durations (`--kernel-trace --stats`)", "",
+          "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for k, (n, avg, mn, mx, pct) in sorted(trace.items(), key=lambda kv: -kv[1][4]):
+        L.append("| %s | %d | %.1f | %.1f | %.1f | %.2f |" % (k[:60], n, avg, mn, mx, pct))
+    L.append("")
+    record = {"workload": w.name, "kernel": "attn_fwd_kernel"}
+    if attn:
+        avg = trace[attn][1]
+        tf = w.flops_per_call / (avg * 1e-6) / 1e12
+        L.append("%s: %.1f us average -> %.1f TFLOP/s (4 N^2 d heads = %.1f GFLOP per launch), %.1f%% of the "
+                 "%.1f TFLOP/s bf16 dense peak (256 CU x 4096 flop/clk x 2.4 GHz)."
+                 % (attn, avg, tf, w.flops_per_call / 1e9, 100 * tf / PEAK_BF16_TFLOPS, PEAK_BF16_TFLOPS))
+        record["avg_launch_us_rocprof"] = avg
+        if bench:
+            rl, ck = bench.get("roofline", {}), bench.get("clock", {})
+            ghz = rl.get("gpu_clock_ghz")
+            if ghz:
+                cus = ck.get("compute_units", 256)
+                peak_c = cus * 4096 * ghz * 1e9 / 1e12
+                cyc = avg * 1e-6 * ghz * 1e9
+                record.update({"gpu_clock_ghz": ghz, "gpu_cycles_per_launch": round(cyc)})
+                L += ["", "GPU clock during this traced run (regen_clock_probe, pure bf16 MFMA load, before and "
+                      "after the timed windows): %.3f GHz. At that clock the MFMA peak is %.1f TFLOP/s, so the "
+                      "kernel runs at %.1f%% of the peak of the clock it ran at; %.3f M GPU cycles per launch."
+                      % (ghz, peak_c, 100 * tf / peak_c, cyc / 1e6)]
+            L += ["", "The same run's bench line (library HIP events on the launch stream, under the profiler): "
+                  "%.3f ms per window of %d calls; attention kernel %.1f us average."
+                  % (bench.get("ms_per_window", float("nan")), w.calls, rl.get("avg_launch_us", float("nan")))]
+    L.append("")
+
+    # traffic
+    fetch, fdur = _counters(os.path.join(run_dir, "fetch"))
+    write, _ = _counters(os.path.join(run_dir, "write"))
+    calf, _ = _counters(os.path.join(run_dir, "calf"))
+    calw, _ = _counters(os.path.join(run_dir, "calw"))
+    if fetch and write and calf and calw:
+        copy_bytes = 512 * (1 << 20)
+        ck = [k for k in calf if "copy" in k.lower() or "elementwise" in k.lower()]
+        fk = calf[ck[0]]["FETCH_SIZE"] if ck else None
+        wk = calw[ck[0]]["WRITE_SIZE"] if ck and ck[0] in calw else None
+        if fk and wk:
+            fs, ws = copy_bytes / (fk * 1024), copy_bytes / (wk * 1024)
+            L += ["## HBM traffic (`--pmc FETCH_SIZE`, `--pmc WRITE_SIZE`, separate runs)", "",
+                  "Calibration: a device copy of 512 MiB reads FETCH_SIZE = %.0f KiB and WRITE_SIZE = %.0f KiB "
+                  "per copy, so FETCH_SIZE is scaled by %.3f and WRITE_SIZE by %.3f." % (fk, wk, fs, ws), "",
+                  "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB | algorithmic MB | ratio |",
+                  "|---|---|---|---|---|---|---|"]
+            algo = {"attn_fwd_kernel": w.bytes_per_call, "rope_k_vt_kernel": w.bytes_per_call}
+            for k in sorted(fetch):
+                if k not in write:
+                    continue
+                fr = fetch[k].get("FETCH_SIZE", 0) * 1024 * fs
+                wr = write[k].get("WRITE_SIZE", 0) * 1024 * ws
+                a = next((v for p_, v in algo.items() if k.startswith(p_)), None)
+                L.append("| %s | %.0f | %.0f | %.1f | %.1f | %s | %s |" % (
+                    k[:60], fetch[k].get("FETCH_SIZE", 0), write[k].get("WRITE_SIZE", 0), fr / 1e6, wr / 1e6,
+                    "%.1f" % (a / 1e6) if a else "-", "%.2f" % ((fr + wr) / a) if a else "-"))
+                if k.startswith("attn_fwd_kernel"):
+                    record.update({"fetch_bytes_per_launch": fr, "write_bytes_per_launch": wr,
+                                   "fetch_scale": fs, "write_scale": ws})
+            L += ["", "Algorithmic bytes: attention reads Q, rotated K and transposed V once and writes O once "
+                  "(4 x heads x N x d x 2 B); the K-rotation / V-transpose pass reads K, V and writes Kr, Vt. "
+                  "Reads above that are K/V blocks fetched again from beyond L2 by workgroups of other XCDs.", ""]
+
+    # instruction / cycle counters
+    sq = {}
+    for pname in ("sq1", "sq2", "sq3"):
+        c, d = _counters(os.path.join(run_dir, pname))
+        k = _pick(c, "attn_fwd_kernel")
+        if k:
+            sq.update(c[k])
+            sq.setdefault("_dispatch_us_" + pname, d.get(k))
+    if sq:
+        L += ["## Instruction and utilisation counters of attn_fwd_kernel (per launch, averaged)", ""]
+        L += ["- %s: %.0f" % (c, v) for c, v in sorted(sq.items()) if not c.startswith("_")]
+        L.append("")
+        xcd = 8
+        gpu_cyc = sq.get("GRBM_GUI_ACTIVE", 0) / xcd
+        busy = sq.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        der = []
+        if gpu_cyc and busy:
+            per_simd = busy / (256 * 4)
+            der.append("MFMA busy %.0f cycles per SIMD of %.0f GPU-busy cycles per XCD (%.1f%%)"
+                       % (per_simd, gpu_cyc, 100 * per_simd / gpu_cyc))
+            dus = sq.get("_dispatch_us_sq1")
+            if dus:
+                der.append("clock in the counter pass %.0f cycles / %.1f us = %.3f GHz" % (gpu_cyc, dus, gpu_cyc / dus / 1e3))
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in sq and busy:
+            der.append("VALU co-issued with MFMA during %.1f%% of MFMA-busy cycles" % (100 * sq["SQ_VALU_MFMA_COEXEC_CYCLES"] / busy))
+        if "SQ_INSTS_MFMA" in sq:
+            need = w.flops_per_call / (2 * 32 * 32 * 16) / 64 * 64
+            der.append("MFMA instructions %.0f vs %.0f needed for 4 N^2 d heads (ratio %.3f, tile padding)"
+                       % (sq["SQ_INSTS_MFMA"], need, sq["SQ_INSTS_MFMA"] / need))
+            if "SQ_INSTS_LDS" in sq:
+                der.append("LDS instructions per MFMA %.3f" % (sq["SQ_INSTS_LDS"] / sq["SQ_INSTS_MFMA"]))
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in sq:
+            der.append("SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = %.1f GFLOP" % (sq["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9))
+        if der:
+            L += ["Derived: " + "; ".join(der) + ".", ""]
+        record["mfma_busy_frac"] = (busy / (256 * 4) / gpu_cyc) if gpu_cyc and busy else None
+    record["kernel_source_sha256"] = kernel_source_sha256()
+    with open(os.path.join(out_dir, "attn_fwd_%s.md" % w.name), "w") as f:
+        f.write("\n".join(L) + "\n")
+    if "fetch_bytes_per_launch" in record:
+        with open(os.path.join(out_dir, "attn_fwd_%s_traffic.json" % w.name), "w") as f:
+            json.dump(record, f, indent=1)
+            f.write("\n")
+
+    # duration tables of the other traced legs
+    for sub in sorted(os.listdir(run_dir)):
+        if sub in ("trace", "fetch", "write", "calf", "calw", "sq1", "sq2", "sq3"):
+            continue
+        st = _stats(os.path.join(run_dir, sub))
+        if not st:
+            continue
+        M = ["# Kernel durations: %s" % sub, "",
+             "rocprofv3 `--kernel-trace --stats`, written by `python bench.py --summarize-rocprof <dir>`. "
+             "Command:", ""]
+        M += ["    " + c for c in cmds if ("/%s " % sub) in c or ("/%s/" % sub) in c] + [""]
+        M += ["| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+        for k, (n, avg, mn, mx, pct) in sorted(st.items(), key=lambda kv: -kv[1][4]):
+            M.append("| %s | %d | %.2f | %.2f | %.2f | %.2f |" % (k[:60], n, avg, mn, mx, pct))
+        with open(os.path.join(out_dir, "%s.md" % sub), "w") as f:
+            f.write("\n".join(M) + "\n")
+    return 0
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -397,6 +683,8 @@ def _cpu_model():
 
 def main():
     args = parse()
+    if args.summarize_rocprof:
+        return summarize_rocprof(args.summarize_rocprof, args.summary_out, args.workload)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -424,7 +712,10 @@ def main():
         print(json.dumps({"workload": w.name, "ulysses": ulysses_leg(w)}), flush=True)
         return 0
     if args.clip_only:
-        print(json.dumps({"workload": w.name, "clip77": clip_leg()}), flush=True)
+        print(json.dumps({"workload": w.name, "clip77": clip_window_leg()}), flush=True)
+        return 0
+    if args.block_window_only:
+        print(json.dumps({"workload": w.name, "block_window": block_window_leg(w)}), flush=True)
         return 0
     if args.ring_split_only:
         qkv = synth.make_qkv(w, 0, 0, device="cuda")
@@ -443,6 +734,7 @@ def main():
         drv.run_window(stream)
     torch.cuda.synchronize()
     print("bench: warmup done", file=sys.stderr, flush=True)
+    clock_before = clock_leg(stream)
 
     # ---- timed region: K whole windows -----------------------------------
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -459,6 +751,10 @@ def main():
     value = drv.flops * args.steps / (ms_total * 1e-3) / 1e12
     print("bench: timed %d windows, %.2f ms/window" % (args.steps, ms_per_window),
           file=sys.stderr, flush=True)
+    clock_after = clock_leg(stream)
+    ghz = 0.5 * (clock_before["gpu_clock_ghz"] + clock_after["gpu_clock_ghz"])
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    peak_at_clock = cus * 4096 * ghz * 1e9 / 1e12  # TFLOP/s at the measured clock
 
     # ---- per-kernel durations from HIP events on the launch stream -------
     prof.profile_read()
@@ -507,7 +803,13 @@ def main():
             "traffic_detail": traffic,
             "avg_launch_us": round(attn_avg_s * 1e6, 2),
             "launches": n_calls,
+            "gpu_clock_ghz": round(ghz, 4),
+            "peak_at_measured_clock": round(peak_at_clock, 1),
+            "frac_at_measured_clock": round(attn_tflops / peak_at_clock, 4),
+            "gpu_cycles_per_launch": round(attn_avg_s * ghz * 1e9),
         },
+        "clock": {"before": clock_before, "after": clock_after, "compute_units": cus,
+                  "window_frac_at_measured_clock": round(value / peak_at_clock, 4)},
         "prep_kernel": {
             "kernel": "rope_k_vt_kernel", "bound": "hbm",
             "avg_launch_us": round(prep_avg_s * 1e6, 2),
@@ -527,8 +829,10 @@ def main():
     drv.close()
     del drv
     torch.cuda.empty_cache()
+    if not args.no_block_window:
+        line["block_window"] = block_window_leg(w)
     if not args.no_clip:
-        line["clip77"] = clip_leg()
+        line["clip77"] = clip_window_leg()
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 oracle sample on the host", file=sys.stderr, flush=True)

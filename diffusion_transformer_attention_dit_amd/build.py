@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libregen_attn.so")
 SOURCES = [os.path.join(CSRC, "regen_attn.hip")]
 DEPENDS = SOURCES + [os.path.join(CSRC, h) for h in ("common.hpp", "attention.hpp", "cross.hpp", "gemm.hpp",
-                                                     "layout.hpp")] + \
+                                                     "layout.hpp", "probe.hpp")] + \
     [os.path.join(INCLUDE, "regen_attn.h")]
 
 HIPCC_FLAGS = [

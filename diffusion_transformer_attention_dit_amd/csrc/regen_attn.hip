@@ -19,6 +19,7 @@
 #include "cross.hpp"
 #include "gemm.hpp"
 #include "layout.hpp"
+#include "probe.hpp"
 
 namespace {
 
@@ -779,6 +780,24 @@ regen_status regen_ulysses_unpack(const void* recv, void* y, int64_t tokens_loca
     regen_status s = ulysses_shape(tokens_local, heads, head_dim, groups, &E);
     if (s != REGEN_OK) return s;
     return block_transpose(recv, y, groups, tokens_local, E, stream);
+}
+
+regen_status regen_clock_probe(int iters, int64_t* counters, double* wall_clock_khz, void* stream) {
+    g_last_error.clear();
+    if (iters < 1 || !counters || !wall_clock_khz)
+        return fail(REGEN_ERR_INVALID_ARGUMENT, "iters must be >= 1; counters and wall_clock_khz non-NULL");
+    if (uintptr_t(counters) % 8 != 0) return fail(REGEN_ERR_INVALID_ARGUMENT, "counters must be 8-byte aligned");
+    int dev = 0, cus = 0, khz = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute");
+    *wall_clock_khz = double(khz);
+    hipLaunchKernelGGL(regen::clock_probe_kernel, dim3(unsigned(std::max(1, cus))), dim3(512), 0,
+                       static_cast<hipStream_t>(stream), reinterpret_cast<long long*>(counters), iters, 0.001f);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip(e, "clock_probe_kernel launch");
+    return REGEN_OK;
 }
 
 regen_status regen_attn_profile_read(regen_attn_t h, double* prep_ms, double* attn_ms,

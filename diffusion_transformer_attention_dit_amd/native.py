@@ -39,6 +39,7 @@ EXPORTS = (
     "regen_attn_workspace_size",
     "regen_attn_profile_read",
     "regen_attn_forward_noalloc",
+    "regen_clock_probe",
 )
 
 # Size of the static device scratch behind regen_attn_forward_noalloc.
@@ -125,6 +126,8 @@ def lib():
     L.regen_attn_profile_read.restype = ctypes.c_int
     L.regen_attn_forward_noalloc.argtypes = [ctypes.POINTER(regen_attn_desc), vp, vp, vp, vp, vp]
     L.regen_attn_forward_noalloc.restype = ctypes.c_int
+    L.regen_clock_probe.argtypes = [ctypes.c_int, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.regen_clock_probe.restype = ctypes.c_int
     _LIB = L
     return L
 
@@ -230,7 +233,37 @@ def regen_attn_profile_read(handle):
     return s, a.value, b.value, c.value, n.value
 
 
+def regen_clock_probe(iters, counters, stream):
+    """Returns (status, wall_clock_khz); counters is an integer device address."""
+    khz = ctypes.c_double(0)
+    s = lib().regen_clock_probe(int(iters), counters, ctypes.byref(khz), stream)
+    return s, khz.value
+
+
 # ---- small convenience wrappers over torch tensors --------------------------
+
+
+def clock_probe(iters=150000, stream=None):
+    """GPU core clock (GHz) under a pure bf16 MFMA load, and that load's
+    TFLOP/s: (ghz, tflops, seconds)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    c = torch.zeros(5, dtype=torch.int64, device="cuda")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    s, khz = regen_clock_probe(iters, c.data_ptr(), stream.cuda_stream)
+    b.record(stream)
+    if s != REGEN_OK:
+        raise RegenAttnError(s, "regen_clock_probe")
+    torch.cuda.synchronize()
+    t0, t1, w0, w1 = (int(x) for x in c[:4].tolist())
+    wall_s = (w1 - w0) / (khz * 1e3)
+    ghz = (t1 - t0) / wall_s / 1e9
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    flops = cus * 8 * iters * 4 * 2 * 32 * 32 * 16
+    secs = a.elapsed_time(b) * 1e-3
+    return ghz, flops / secs / 1e12, secs
 
 def ulysses_pack(x, groups, out=None, stream=None):
     """x [tokens_local, heads, d] bf16 -> [groups, tokens_local, heads/groups, d]."""

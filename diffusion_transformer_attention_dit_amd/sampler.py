@@ -50,3 +50,43 @@ class WindowDriver:
 
     def close(self):
         self.attn.close()
+
+
+class BlockWindowDriver:
+    """One decode window of whole self-attention blocks: four steps x 30
+    blocks of [Q|K|V] = X W_qkv^T, 3D-RoPE attention, Y = O W_o^T. Block b
+    has its own random-init weights (the same in every step, as a trained
+    model's would be); every (step, block) call gets its own seeded hidden
+    states X, all drawn before timing starts."""
+
+    def __init__(self, workload: synth.Workload, device="cuda", base_seed=0, steps=None, blocks=None):
+        from .native import Block
+        self.w = workload
+        self.steps = steps if steps is not None else workload.steps
+        self.blocks = blocks if blocks is not None else workload.blocks
+        self.blk = Block(workload.heads, workload.head_dim, workload.grid)
+        self.weights = []
+        for b in range(self.blocks):
+            _, w_qkv, w_o = synth.make_block_inputs(workload, 0, b, device=device, base_seed=base_seed)
+            self.weights.append((w_qkv, w_o))
+        self.xs = [synth.make_block_inputs(workload, s, b, device=device, base_seed=base_seed)[0]
+                   for s in range(self.steps) for b in range(self.blocks)]
+        self.outs = [torch.empty_like(self.xs[0]) for _ in range(2)]
+
+    @property
+    def calls(self):
+        return self.steps * self.blocks
+
+    @property
+    def flops(self):
+        """Attention (4 N^2 d heads) plus both projections (2 N hidden 4 hidden) per call."""
+        hid = self.w.heads * self.w.head_dim
+        return self.calls * (self.w.flops_per_call + 2 * self.w.tokens * hid * 4 * hid)
+
+    def run_window(self, stream=None):
+        for i, x in enumerate(self.xs):
+            w_qkv, w_o = self.weights[i % self.blocks]
+            self.blk.forward(x, w_qkv, w_o, out=self.outs[i & 1], stream=stream)
+
+    def close(self):
+        self.blk.close()

@@ -337,6 +337,19 @@ regen_status regen_attn_profile_read(regen_attn_t h, double *prep_ms, double *at
                                      double *merge_ms, int64_t *calls);
 
 /*
+ * Measurement aid: the GPU core clock under a pure bf16 MFMA load (one
+ * workgroup of 8 waves per compute unit, every wave issuing iters rounds of
+ * four independent 32x32x16 MFMAs). Enqueues one kernel on `stream` that
+ * writes, from one wave, counters[0..1] = core cycle counter at the start
+ * and end of its loop and counters[2..3] = constant-rate counter at start
+ * and end (counters: device memory, 5 int64, 8-byte aligned, caller-owned;
+ * counters[4] is scratch). *wall_clock_khz receives the constant counter's
+ * rate. After the stream has finished: clock = (c1 - c0) / ((c3 - c2) /
+ * (wall_clock_khz * 1e3)). Errors: INVALID_ARGUMENT, HIP.
+ */
+regen_status regen_clock_probe(int iters, int64_t *counters, double *wall_clock_khz, void *stream);
+
+/*
  * Bytes of the rotated-K / transposed-V workspace regen_attn_create would
  * allocate for desc (the device-dependent split-tile scratch not included),
  * or 0 if the description is invalid. Touches no device.
