@@ -27,6 +27,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 left at their maximum).
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // Logical block id with consecutive ids on one XCD. Blocks are dispatched
 // round-robin over the 8 XCDs (block b runs on XCD b % 8); this maps each
 // XCD's blocks onto one contiguous range of logical ids, so that the blocks

@@ -13,10 +13,6 @@ namespace regen {
 
 constexpr int kCrossMaxKeys = 256;  // longest context held in LDS
 
-// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
-// in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 left at their maximum).
-constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 // ---------------------------------------------------------------------------
 // cross_attn_kernel: grid G, NW * 64 threads.
 //   q, o    : bf16, row m of head h at element h * qh + m * qn of q and

@@ -171,14 +171,18 @@ __device__ __forceinline__ void gemm8_issue(__amdgpu_buffer_rsrc_t rs, int ld, i
     }
 }
 
-// One (4 WTM) x (2 WTN) tile at (m0, n0) by 8 waves (WTM x WTN each). Ends
-// with every wave past its last read of `smem`.
-template <int WTM, int WTN>
+// One (4 WTM) x (2 WTN) tile at (m0, n0) by 8 waves (WTM x WTN each), K
+// steps through STAGES LDS buffers (STAGES * SBYTES <= 128 KiB): two for
+// the full tiles, more for the small tiles of a last round, whose steps are
+// too short to hide a copy's latency behind one step of work. Ends with
+// every wave past its last read of `smem`.
+template <int WTM, int WTN, int STAGES = 2>
 __device__ __forceinline__ void gemm8_tile(__amdgpu_buffer_rsrc_t ra, int lda, __amdgpu_buffer_rsrc_t rb,
                                            int ldb, uint16_t* __restrict__ C, int ldc, int M, int N, int K,
                                            int m0, int n0, char* smem) {
     constexpr int TM = 4 * WTM, TN = 2 * WTN, NBM = WTM / 32, NBN = WTN / 32;
     constexpr int ABYTES = TM * kGemmBK * 2, SBYTES = (TM + TN) * kGemmBK * 2;
+    static_assert(STAGES >= 2 && STAGES * SBYTES <= kGemmBigSmem, "LDS stages");
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31, half = lane >> 5;
     const int wm = wave >> 1, wn = wave & 1;
@@ -190,20 +194,8 @@ __device__ __forceinline__ void gemm8_tile(__amdgpu_buffer_rsrc_t ra, int lda, _
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    gemm8_issue<TM>(ra, lda, m0, 0, smem, wave, lane);
-    gemm8_issue<TN>(rb, ldb, n0, 0, smem + ABYTES, wave, lane);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
     const int nk = K / kGemmBK;
-    for (int kt = 0; kt < nk; ++kt) {
-        char* cur = smem + (kt & 1) * SBYTES;
-        if (kt + 1 < nk) {
-            char* nxt = smem + ((kt + 1) & 1) * SBYTES;
-            gemm8_issue<TM>(ra, lda, m0, (kt + 1) * kGemmBK, nxt, wave, lane);
-            gemm8_issue<TN>(rb, ldb, n0, (kt + 1) * kGemmBK, nxt + ABYTES, wave, lane);
-        }
-        const char* as = cur;
-        const char* bs = cur + ABYTES;
+    auto mma_step = [&](const char* as, const char* bs) {
 #pragma unroll
         for (int kk = 0; kk < kGemmBK / 16; ++kk) {
             bf16x8 a[NBM], b[NBN];
@@ -219,8 +211,51 @@ __device__ __forceinline__ void gemm8_tile(__amdgpu_buffer_rsrc_t ra, int lda, _
                 for (int j = 0; j < NBN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
         }
+    };
+    if constexpr (STAGES > 2) {
+        // Copies run STAGES - 1 steps ahead. Step kt: wait for this wave's
+        // copies of step kt (those of the later steps already issued may stay
+        // in flight: CP copies per step per wave), barrier (every wave's
+        // copies of kt have landed and every wave is past step kt - 1, whose
+        // buffer the copies of step kt + STAGES - 1 now reuse), compute.
+        constexpr int CP = TM / 64 + TN / 64;
+        for (int s = 0; s < STAGES - 1 && s < nk; ++s) {
+            gemm8_issue<TM>(ra, lda, m0, s * kGemmBK, smem + s * SBYTES, wave, lane);
+            gemm8_issue<TN>(rb, ldb, n0, s * kGemmBK, smem + s * SBYTES + ABYTES, wave, lane);
+        }
+        for (int kt = 0; kt < nk; ++kt) {
+            const int later = min(STAGES - 2, nk - 1 - kt);  // steps issued after kt
+            static_assert(STAGES <= 5 && 3 * CP < 64, "wait counts below");
+            if (later >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_only(3 * CP));
+            else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * CP));
+            else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(CP));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+            __builtin_amdgcn_s_barrier();
+            if (kt + STAGES - 1 < nk) {
+                char* nxt = smem + ((kt + STAGES - 1) % STAGES) * SBYTES;
+                gemm8_issue<TM>(ra, lda, m0, (kt + STAGES - 1) * kGemmBK, nxt, wave, lane);
+                gemm8_issue<TN>(rb, ldb, n0, (kt + STAGES - 1) * kGemmBK, nxt + ABYTES, wave, lane);
+            }
+            const char* cur = smem + (kt % STAGES) * SBYTES;
+            mma_step(cur, cur + ABYTES);
+        }
+        __syncthreads();
+    } else {
+        gemm8_issue<TM>(ra, lda, m0, 0, smem, wave, lane);
+        gemm8_issue<TN>(rb, ldb, n0, 0, smem + ABYTES, wave, lane);
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            char* cur = smem + (kt & 1) * SBYTES;
+            if (kt + 1 < nk) {
+                char* nxt = smem + ((kt + 1) & 1) * SBYTES;
+                gemm8_issue<TM>(ra, lda, m0, (kt + 1) * kGemmBK, nxt, wave, lane);
+                gemm8_issue<TN>(rb, ldb, n0, (kt + 1) * kGemmBK, nxt + ABYTES, wave, lane);
+            }
+            mma_step(cur, cur + ABYTES);
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
     }
     const bool st8 = (ldc & 3) == 0;
 #pragma unroll
@@ -276,7 +311,7 @@ __global__ __launch_bounds__(512) void gemm_nt256_kernel(const uint16_t* __restr
         if (pid < left * 8) {
             int m0, n0;
             origin(done + pid / 8, &m0, &n0);
-            gemm8_tile<32, 32>(ra, lda, rb, ldb, C, ldc, M, N, K, m0 + ((pid & 7) >> 2) * 128,
+            gemm8_tile<32, 32, 4>(ra, lda, rb, ldb, C, ldc, M, N, K, m0 + ((pid & 7) >> 2) * 128,
                                n0 + (pid & 3) * 64, smem);
         }
         return;
@@ -284,7 +319,7 @@ __global__ __launch_bounds__(512) void gemm_nt256_kernel(const uint16_t* __restr
     for (int qd = pid; qd < left * 4; qd += G) {
         int m0, n0;
         origin(done + qd / 4, &m0, &n0);
-        gemm8_tile<32, 64>(ra, lda, rb, ldb, C, ldc, M, N, K, m0 + ((qd & 3) >> 1) * 128,
+        gemm8_tile<32, 64, 4>(ra, lda, rb, ldb, C, ldc, M, N, K, m0 + ((qd & 3) >> 1) * 128,
                            n0 + (qd & 1) * 128, smem);
     }
 }
