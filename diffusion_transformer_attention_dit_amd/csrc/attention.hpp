@@ -40,6 +40,7 @@ namespace regen {
 
 constexpr int kPrepKeys = 128;  // workspace padding unit (keys)
 constexpr int kPrepBlock = 64;  // keys per rope_k_vt block: one Kr / Vt tile
+constexpr int kTabLds = 3072;   // (cos, sin) entries the attention kernel keeps in LDS
 
 // Rotary geometry: latent grid, pairs per axis, offsets of each axis' table
 // in the (cos, sin) table. Entry off[a] + pos * pairs[a] + j holds
@@ -310,6 +311,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // The next segment's Q rows, copied during the current segment: row r at
     // byte r * 2 D, 16-byte chunk c stored at position c ^ (r % (D / 8)).
     __shared__ __attribute__((aligned(1024))) char qsm[BM * D * 2];
+    // The (cos, sin) table, when it fits: Q rows are rotated from LDS, with no
+    // global load waiting behind the K / V copies in flight.
+    __shared__ float2 tabsm[kTabLds];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -323,6 +327,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     const uint32_t head_bytes = (uint32_t)Npad * D * 2;
     const int HW = geo.H * geo.W;
+    const int tab_n = geo.off[2] + geo.W * geo.pairs[2];  // table entries
+    const bool tab_lds = rotate_q && tab_n <= kTabLds;    // uniform
+    if (tab_lds)  // read after the barrier before the first segment's Q
+        for (int i = tid; i < tab_n; i += NW * 64) tabsm[i] = tab[i];
 
     // Buffer resources over the Kr rows and Vt blocks of tile tt's head.
     auto head_rsrc = [&](int tt, __amdgpu_buffer_rsrc_t* krs, __amdgpu_buffer_rsrc_t* vrs) {
@@ -357,6 +365,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     __amdgpu_buffer_rsrc_t krs, vrs;
     head_rsrc(t, &krs, &vrs);
+    if (q_lds) issue_q(t);
     issue_tile<D, BN, NW>(krs, vrs, kv0, smem, smem + KBYTES, wave, lane);
     int buf = 0;
     bool more = true;
@@ -373,34 +382,55 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // Q: load this lane's half-rows, rotate them (RoPE on load) and fold
         // in the softmax scale and log2(e), so that Q K^T comes out in the
         // exp2 domain.
+        if (k == 0) {  // the first tile's Q rows, the table and the first K / V tile
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
         bf16x8 qf[D / 16];
         {
             const int qn = qrow < Nq ? qrow : 0;
             const int qg = q_off + qn;  // token index on the grid
             const int tt = qg / HW, hh = (qg / geo.W) % geo.H, ww = qg % geo.W;
-            const uint16_t* qp = q + hd * qh + qn * qn_stride + half * 8;
-            // From LDS when the previous segment prefetched this tile's rows.
-            const bool from_lds = q_lds && k > 0;
             const int lr = wave * 32 + col;
+            char* qrow_sm = qsm + lr * D * 2;
+            if (!q_lds) {
+                // Rows too far apart for one buffer resource: each wave
+                // stages its own rows (zero past the end) into the same LDS
+                // layout; the wave's LDS accesses complete in order.
+                const uint16_t* qp = q + hd * qh + (long long)qn * qn_stride + half * 8;
 #pragma unroll
-            for (int kb = 0; kb < D / 16; ++kb) {
-                uint4 x = make_uint4(0, 0, 0, 0);
-                if (qrow < Nq) {
-                    if (from_lds)
-                        x = *reinterpret_cast<const uint4*>(qsm + lr * D * 2 + ((kb * 2 + half) ^ (lr % QCPR)) * 16);
-                    else
-                        x = *reinterpret_cast<const uint4*>(qp + kb * 16);
-                    if (rotate_q) {
-                        x = rope_chunk(x, tab, geo, kb * 8 + half * 4, tt, hh, ww, c2);
-                    } else {  // unrotated (cross-attention): scale and round only
-                        const uint32_t src[4] = {x.x, x.y, x.z, x.w};
-                        uint32_t dst[4];
-#pragma unroll
-                        for (int p = 0; p < 4; ++p) dst[p] = pack_bf16(bf_lo(src[p]) * c2, bf_hi(src[p]) * c2);
-                        x = make_uint4(dst[0], dst[1], dst[2], dst[3]);
-                    }
+                for (int kb = 0; kb < D / 16; ++kb) {
+                    const uint4 x = qrow < Nq ? *reinterpret_cast<const uint4*>(qp + kb * 16) : make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4*>(qrow_sm + ((kb * 2 + half) ^ (lr % QCPR)) * 16) = x;
                 }
-                qf[kb] = __builtin_bit_cast(bf16x8, x);
+            }
+            // Every chunk is requested before any is used; rows past the end
+            // are zero in LDS.
+            uint4 xq[D / 16];
+#pragma unroll
+            for (int kb = 0; kb < D / 16; ++kb)
+                xq[kb] = *reinterpret_cast<const uint4*>(qrow_sm + ((kb * 2 + half) ^ (lr % QCPR)) * 16);
+            // One instance per table location, so that the LDS one reads
+            // through LDS addresses (a generic pointer would wait on every
+            // outstanding global copy too).
+            auto rotate = [&](const float2* tb) {
+#pragma unroll
+                for (int kb = 0; kb < D / 16; ++kb)
+                    qf[kb] = __builtin_bit_cast(bf16x8, rope_chunk(xq[kb], tb, geo, kb * 8 + half * 4, tt, hh, ww, c2));
+            };
+            if (tab_lds) {
+                rotate(tabsm);
+            } else if (rotate_q) {
+                rotate(tab);
+            } else {  // unrotated (cross-attention): scale and round only
+#pragma unroll
+                for (int kb = 0; kb < D / 16; ++kb) {
+                    const uint32_t src[4] = {xq[kb].x, xq[kb].y, xq[kb].z, xq[kb].w};
+                    uint32_t dst[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) dst[p] = pack_bf16(bf_lo(src[p]) * c2, bf_hi(src[p]) * c2);
+                    qf[kb] = __builtin_bit_cast(bf16x8, make_uint4(dst[0], dst[1], dst[2], dst[3]));
+                }
             }
         }
 
@@ -417,11 +447,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int i = 0; i < 16; ++i) negm[i] = 0.0f;
         float l0 = 0.0f, l1 = 0.0f;  // this lane's partial row sums
-
-        if (k == 0) {
-            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-        }
 
         for (int b = kv0; b < kv1; ++b) {
             const char* ks = smem + buf * (KBYTES + VBYTES);
@@ -447,7 +472,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             // Vt fragments are requested after the S products, to land during
             // the softmax.
             constexpr int KB = D / 16, NK = (BN / 32) * KB, QB16 = BN / 16, NV = (D / 32) * QB16;
-            constexpr int RING = 8;
+            constexpr int RING = 8, DB = D / 32;
+            // The P V products run key group by key group (c = kq DB + db), so
+            // that each group's P is needed only by its own DB products.
+            auto vfrag = [](int c) { return (c % DB) * QB16 + c / DB; };
             auto frag = [&](int f) -> bf16x8 {
                 return *reinterpret_cast<const bf16x8*>(ks + f * 1024 + lane * 16);
             };
@@ -469,7 +497,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 if (f + RING < NK) fr[f % RING] = frag(f + RING);
             }
 #pragma unroll
-            for (int f = NK; f < NK + RING; ++f) fr[f % RING] = frag(f);
+            for (int c = 0; c < RING; ++c) fr[(NK + c) % RING] = frag(NK + vfrag(c));
 
             __builtin_amdgcn_s_setprio(0);
             // Keys past the end of the sequence get -inf (never zero-padding).
@@ -525,34 +553,52 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
 
             // P = exp2(s), rounded to bf16 for the second product; the row sum
-            // accumulates the rounded values (v_dot2 with ones).
+            // accumulates the rounded values (v_dot2 with ones). Key group kq
+            // (16 keys) of P is computed while the products of group kq - 1
+            // run.
             bf16x8 pk[BN / 16];
             const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+            auto make_p = [&](int kq) {
+                const int kk = kq / 2, hb = kq % 2;
+                uint32_t w4[4];
 #pragma unroll
-            for (int kk = 0; kk < BN / 32; ++kk)
-#pragma unroll
-                for (int hb = 0; hb < 2; ++hb) {
-                    uint32_t w4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float e0 = __builtin_amdgcn_exp2f(s[kk][hb * 8 + 2 * e]);
-                        const float e1 = __builtin_amdgcn_exp2f(s[kk][hb * 8 + 2 * e + 1]);
-                        w4[e] = pack_bf16(e0, e1);
-                        if (e & 1)
-                            l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[e]), ones, l1, false);
-                        else
-                            l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[e]), ones, l0, false);
-                    }
-                    pk[kk * 2 + hb] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+                for (int e = 0; e < 4; ++e) {
+                    const float e0 = __builtin_amdgcn_exp2f(s[kk][hb * 8 + 2 * e]);
+                    const float e1 = __builtin_amdgcn_exp2f(s[kk][hb * 8 + 2 * e + 1]);
+                    w4[e] = pack_bf16(e0, e1);
+                    if (e & 1)
+                        l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[e]), ones, l1, false);
+                    else
+                        l0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[e]), ones, l0, false);
                 }
+                pk[kq] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+            };
 
             // O^T += V^T P^T.
+            make_p(0);
 #pragma unroll
-            for (int g = 0; g < NV; ++g) {
-                const int f = NK + g, db = g / QB16, kq = g % QB16;
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % RING], pk[kq], acc[db], 0, 0, 0);
-                if (f + RING < NK + NV) fr[f % RING] = frag(f + RING);
+            for (int kq = 0; kq < QB16; ++kq) {
+                if (kq + 1 < QB16) make_p(kq + 1);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int c = kq * DB + db;
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[(NK + c) % RING], pk[kq], acc[db], 0, 0, 0);
+                    if (c + RING < NV) fr[(NK + c) % RING] = frag(NK + vfrag(c + RING));
+                }
             }
+#ifdef REGEN_PV_HINTS
+            // Issue order: group 0's P, then each product followed by a share
+            // of the next group's P and one operand read.
+            __builtin_amdgcn_sched_group_barrier(0x402, 16, 0);
+#pragma unroll
+            for (int c = 0; c < NV - DB; ++c) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x402, 16 / DB, 0);
+                if constexpr (NV > RING) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int c = 0; c < DB; ++c) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#endif
 
             // The next block's copies must have landed (this wave's: vmcnt;
             // the others': the barrier) before anyone reads them, and every
