@@ -27,8 +27,8 @@ constexpr int kCrossMaxKeys = 256;  // longest context held in LDS
 // Kr / Vt fragment layout of rope_k_vt_kernel, in tiles of 32 keys (K
 // gathered by the copies themselves, V copied row by row and transposed in
 // LDS), then its waves take the head's units in turn, each unit
-// independently: Q to registers (two units' Q loads kept in flight ahead of
-// the one computing), S^T = K Q^T and online softmax over the key tiles
+// independently: Q to registers (the next unit's Q loads in flight while
+// one computes), S^T = K Q^T and online softmax over the key tiles
 // exactly as in attn_fwd_kernel, O^T = V^T P^T, O / l stored.
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool LSE>
@@ -257,9 +257,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                         smem + j * TBYTES + KBYTES + (R % NVF) * 1024);
             }
         }
-        // This wave's units u0 + wave + i NW, two in flight: the loads of the
-        // unit after next go out as soon as a unit's Q is in registers. The
-        // first two units' loads go out behind the context copies, whose wait
+        // This wave's units u0 + wave + i NW, one ahead: the next unit's Q
+        // loads go out as soon as a unit's Q is in registers, so the stores
+        // of the first units overlap the loads of the later ones (requesting
+        // two units' Q up front had every wave's loads ahead of any store).
+        // The first unit's loads go out behind the context copies, whose wait
         // leaves them outstanding (the counter retires in issue order).
         const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + h * qh, q_bytes);
         const __amdgpu_buffer_rsrc_t ors = make_rsrc(o + h * oh, o_bytes);
@@ -269,8 +271,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         long long u = u0 + wave;
         uint4 qa[D / 16], qb[D / 16];
         load_q(qa, qrs, h, u, seg_end);
-        load_q(qb, qrs, h, u + NW, seg_end);
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * QL));
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(QL));
         __syncthreads();
         // Vt fragment 4 db + kq of tile j from the raw rows: lane (c, g)
         // holds head dim 32 db + c of the keys in slots 8 g .. 8 g + 7 of key
@@ -304,25 +305,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
         __syncthreads();
 
-        // Outstanding operations (oldest first) at each wait; the first pass
-        // has no earlier unit's stores or loads behind the one awaited.
+        // Outstanding operations (oldest first) at each wait: behind qa, the
+        // last pass's stores of B (none on the first pass, whose context
+        // copies were awaited above); behind qb, A's stores.
         bool first = true;
         for (; u < seg_end; u += 2 * NW) {
             bf16x8 qf[D / 16];
-            // qa: behind it qb (first pass) or the last pass's stores of A,
-            // qb loads and stores of B.
-            if (first) __builtin_amdgcn_s_waitcnt(vmcnt_only(QL));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * ST + QL));
+            if (first) __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_only(ST));
             scale_q(qa, qf);
-            load_q(qa, qrs, h, u + 2 * NW, seg_end);
+            load_q(qb, qrs, h, u + NW, seg_end);
             unit(qf, ors, lrs, h, u);
             if (u + NW >= seg_end) break;
-            // qb: behind it the new qa loads and A's stores (and, after the
-            // first pass, the last pass's stores of B).
-            if (first) __builtin_amdgcn_s_waitcnt(vmcnt_only(QL + ST));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * ST + QL));
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(ST));
             scale_q(qb, qf);
-            load_q(qb, qrs, h, u + 3 * NW, seg_end);
+            load_q(qa, qrs, h, u + 2 * NW, seg_end);
             unit(qf, ors, lrs, h, u + NW);
             first = false;
         }

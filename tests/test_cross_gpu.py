@@ -36,9 +36,10 @@ def check_o(got, ref, label):
     assert ma <= MAX_ABS and mr <= MEAN_REL, (label, ma, mr)
 
 
-# 1..256 run in the short-context kernel (256: four full key tiles), 257 and
+# 1..256 run in the short-context kernel (up to 128 with its O rows staged
+# through LDS; 256: eight full key tiles), 257 and
 # up in the persistent one.
-@pytest.mark.parametrize("ctx_len", [1, 64, 77, 226, 256, 257, 512, 1000])
+@pytest.mark.parametrize("ctx_len", [1, 64, 77, 128, 129, 226, 256, 257, 512, 1000])
 def test_cross_block_all_elements(ctx_len):
     w = synth.WORKLOADS["block_12x128_n1560"]
     say("case cross-attention block, ctx %d" % ctx_len)
@@ -69,7 +70,7 @@ def test_cross_window_sampled(ctx_len):
     check_o(f64(o)[:, rows], ref, "cross window %d" % ctx_len)
 
 
-@pytest.mark.parametrize("ctx_len", [1, 77, 200, 300])
+@pytest.mark.parametrize("ctx_len", [1, 77, 128, 129, 200, 300])
 def test_cross_head_dim_64(ctx_len):
     # head_dim 64 (one head, 1560 tokens); contexts up to 256 keys run in the
     # short-context kernel, longer ones in the persistent one.
