@@ -534,7 +534,8 @@ def summarize_rocprof(run_dir, out_dir, workload="window25_12x128_n10920"):
          "bench.py, all in one GPU session; this file and the traffic record beside it were written by "
          "`python bench.py --summarize-rocprof <dir>` from the passes' CSV output. Commands (run from "
          "/tmp with TMPDIR=/tmp; $REPO is the repository root):", ""]
-    L += ["    " + c for c in cmds] + [""]
+    own = ("trace", "fetch", "write", "calf", "calw", "sq1", "sq2", "sq3")
+    L += ["    " + c for c in cmds if any(("/%s " % sub) in c or ("/%s/" % sub) in c for sub in own)] + [""]
     trace = _stats(os.path.join(run_dir, "trace"))
     bench = None
     bpath = os.path.join(run_dir, "trace", "bench.json")
