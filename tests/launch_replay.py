@@ -20,6 +20,7 @@ import numpy as np
 
 KBM, KBN, KNW = 256, 64, 8          # attention: query rows per tile, keys per block, waves
 PREP_KEYS, PREP_BLOCK = 128, 64     # workspace padding unit, keys per rope_k_vt block
+TAB_LDS = 3072                      # (cos, sin) entries attn_fwd_kernel keeps in LDS
 GEMM_TILE, GEMM_BK, GEMM_BIG = 128, 64, 256
 LDS_BYTES = 160 * 1024
 
@@ -153,7 +154,8 @@ def attention_call(buf, *, heads, D, nq, nk, tokens_pad, P, q_name, q_base, qh, 
     # attn_fwd_kernel: persistent grid of P workgroups.
     KBYTES = KBN * D * 2
     BM = KBM
-    assert 2 * (2 * KBYTES) + BM * D * 2 <= LDS_BYTES, "LDS of attn_fwd_kernel"
+    # K / Vt double buffer, the Q rows of the next tile, the (cos, sin) table
+    assert 2 * (2 * KBYTES) + BM * D * 2 + TAB_LDS * 8 <= LDS_BYTES, "LDS of attn_fwd_kernel"
     head_bytes = Npad * D * 2
     covered = np.zeros((heads * sc["n_qtiles"], sc["nkv"]), dtype=np.int32)
     slots = {}
