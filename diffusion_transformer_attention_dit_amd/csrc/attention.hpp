@@ -99,7 +99,8 @@ __device__ __forceinline__ uint4 rope_chunk(uint4 in, const float2* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// rope_k_vt_kernel: K rotation + V transpose. Grid (Npad / 64, heads), 256 threads.
+// rope_k_vt_kernel: K rotation + V transpose. Grid (Npad / 64, heads, D / 64),
+// 256 threads.
 //   k, v : bf16, key n of head h at element h * sh + n * sn (head-major
 //          [heads][N][D]: sh = N D, sn = D; token-major [N][heads][D]:
 //          sh = D, sn = heads D), key n being token n_off + n of the grid.
@@ -120,16 +121,23 @@ __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     int n_off, long long sh, long long sn) {
     const int hd = blockIdx.y;
     const int n0 = blockIdx.x * kPrepBlock;
+    const int z = blockIdx.z;  // head dims 64 z .. 64 z + 63 of the tile
     const int HW = geo.H * geo.W;
 
     // Rows are staged through LDS so that both the reads of K and V (whole
-    // rows) and the writes of Kr and Vt (whole 1 KiB fragments) are
-    // contiguous. LDS rows are XOR-swizzled by 16-byte chunk.
-    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    // 128-byte row halves) and the writes of Kr and Vt (whole 1 KiB
+    // fragments) are contiguous. LDS rows are XOR-swizzled by 16-byte chunk.
+    // A block takes 64 of the head dims: the Kr fragments of 16-dim blocks
+    // 4 z .. 4 z + 3 and the Vt fragments of 32-dim blocks 2 z, 2 z + 1 are
+    // the tile's fragments 8 z .. 8 z + 7 of each, so the grid has D / 64
+    // blocks per tile and twice as many blocks reach the memory system at
+    // D = 128 (a short call, such as three heads, does not fill the chip
+    // with one block per tile).
+    constexpr int DH = 64;                // head dims per block
+    constexpr int CPR = DH / 8;           // 16-byte chunks per staged row
     constexpr int PER = kPrepBlock * CPR / 256;
-    constexpr int NK = D / 8;              // 1 KiB fragments per 64-key Kr tile
-    constexpr int NV = (D / 32) * 4;       // 1 KiB fragments per 64-key Vt tile
-    static_assert(NK * 64 == PER * 256 && NV * 64 == PER * 256, "fragments per block");
+    constexpr int NF = 8;                 // 1 KiB fragments of Kr (and of Vt) per block
+    static_assert(D % DH == 0 && NF * 64 == PER * 256, "fragments per block");
     __shared__ uint4 kl[kPrepBlock * CPR];
     __shared__ uint4 vl[kPrepBlock * CPR];
     const int tid = threadIdx.x;
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     uint4 kin[PER], vin[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int cid = i * 256 + tid, r = cid / CPR, c = cid % CPR, n = n0 + r;
+        const int cid = i * 256 + tid, r = cid / CPR, c = z * CPR + cid % CPR, n = n0 + r;
         kin[i] = make_uint4(0, 0, 0, 0);
         vin[i] = make_uint4(0, 0, 0, 0);
         if (n < N) {
@@ -148,43 +156,42 @@ __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int cid = i * 256 + tid, r = cid / CPR, c = cid % CPR, n = n0 + r;
+        const int cid = i * 256 + tid, r = cid / CPR, cl = cid % CPR, n = n0 + r;
         uint4 out = make_uint4(0, 0, 0, 0);
         if (n < N) {
             const int ng = n_off + n;  // token index on the grid
             const int t = ng / HW, h = (ng / geo.W) % geo.H, w = ng % geo.W;
-            out = rope_chunk(kin[i], tab, geo, c * 4, t, h, w);
+            out = rope_chunk(kin[i], tab, geo, (z * CPR + cl) * 4, t, h, w);
         }
-        kl[sw(r, c)] = out;
-        vl[sw(r, c)] = vin[i];
+        kl[sw(r, cl)] = out;
+        vl[sw(r, cl)] = vin[i];
     }
     __syncthreads();
 
-    // Fragment F = tile * NK + f of Kr (f = 2 kb + kk): lane (c, g) holds key
-    // 32 kk + c, head dims 16 kb + 8 g .. + 7. Fragment F = tile * NV + gp of
-    // Vt (gp = 4 db + kq): lane (c, g) holds head dim 32 db + c of the keys
-    // in slots 8 g .. 8 g + 7 of key group kq.
+    // Tile fragment 8 z + F of Kr (f = 2 kb + kk): lane (c, g) holds key
+    // 32 kk + c, head dims 16 kb + 8 g .. + 7. Tile fragment 8 z + F of Vt
+    // (4 db + kq): lane (c, g) holds head dim 32 db + c of the keys in slots
+    // 8 g .. 8 g + 7 of key group kq.
     const int lane = tid & 63, c = lane & 31, g = lane >> 5;
-    uint16_t* kdst = kr + ((size_t)hd * Npad + n0) * D;
-    uint16_t* vdst = vt + ((size_t)hd * Npad + n0) * D;
+    uint16_t* kdst = kr + ((size_t)hd * Npad + n0) * D + z * NF * 512;
+    uint16_t* vdst = vt + ((size_t)hd * Npad + n0) * D + z * NF * 512;
     const uint16_t* vl16 = reinterpret_cast<const uint16_t*>(vl);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int F = i * 4 + (tid >> 6);
         {
-            const int tl = F / NK, f = F % NK;
-            const int r = tl * 64 + (f % 2) * 32 + c;
-            *reinterpret_cast<uint4*>(kdst + F * 512 + lane * 8) = kl[sw(r, (f / 2) * 2 + g)];
+            const int r = (F % 2) * 32 + c;
+            *reinterpret_cast<uint4*>(kdst + F * 512 + lane * 8) = kl[sw(r, (F / 2) * 2 + g)];
         }
         {
-            const int tl = F / NV, gp = F % NV, d = (gp / 4) * 32 + c;
-            const int rb = tl * 64 + (gp % 4) * 16 + 4 * g;
+            const int dl = (F / 4) * 32 + c;  // head dim 64 z + dl
+            const int rb = (F % 4) * 16 + 4 * g;
             uint32_t w4[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r0 = rb + (m / 2) * 8 + (m % 2) * 2, r1 = r0 + 1;
-                const uint32_t lo = vl16[sw(r0, d >> 3) * 8 + (d & 7)];
-                const uint32_t hi = vl16[sw(r1, d >> 3) * 8 + (d & 7)];
+                const uint32_t lo = vl16[sw(r0, dl >> 3) * 8 + (dl & 7)];
+                const uint32_t hi = vl16[sw(r1, dl >> 3) * 8 + (dl & 7)];
                 w4[m] = lo | (hi << 16);
             }
             *reinterpret_cast<uint4*>(vdst + F * 512 + lane * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);

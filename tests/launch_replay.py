@@ -135,21 +135,27 @@ def attention_call(buf, *, heads, D, nq, nk, tokens_pad, P, q_name, q_base, qh, 
     if sc is None:
         raise OutOfBounds("too many units")
 
-    # rope_k_vt_kernel: grid (Npad / 64, heads), one 64-key tile per block.
-    CPR = D // 8
+    # rope_k_vt_kernel: grid (Npad / 64, heads, D / 64), one 64-key tile and 64
+    # head dims per block: reads the keys' chunks 8 z .. 8 z + 7 (16 bytes each)
+    # and writes fragments 8 z .. 8 z + 7 of the tile's Kr and of its Vt.
+    CPR = 8                            # 16-byte chunks of the 64 dims a block stages
+    PER = PREP_BLOCK * CPR // 256
+    assert D % 64 == 0
     for hd in range(heads):
         n = np.arange(nk, dtype=np.int64)  # keys read (n < N)
-        for name, base in ((k_name, k_base), (v_name, v_base)):
-            off = base + hd * kh + n * kn
-            buf.access(name, off.min(), off.max() + D, "rope_k_vt read")
-        # write: (hd Npad + n0) D + F 512 + lane 8 + 8, F < 4 PER, per tile
-        PER = PREP_BLOCK * CPR // 256
-        last_tile = Npad // PREP_BLOCK - 1
-        hi = (hd * Npad + last_tile * PREP_BLOCK) * D + (4 * PER - 1) * 512 + 63 * 8 + 8
-        lo = hd * Npad * D
-        buf.access("kr", lo, hi, "rope_k_vt Kr write")
-        buf.access("vt", lo, hi, "rope_k_vt Vt write")
+        for z in range(D // 64):
+            for name, base in ((k_name, k_base), (v_name, v_base)):
+                off = base + hd * kh + n * kn + z * 64
+                buf.access(name, off.min(), off.max() + 64, "rope_k_vt read")
+            # write: (hd Npad + n0) D + 8 z 512 + F 512 + lane 8 + 8, F < 4 PER
+            last_tile = Npad // PREP_BLOCK - 1
+            for tile in (0, last_tile):
+                base_t = (hd * Npad + tile * PREP_BLOCK) * D + z * 8 * 512
+                buf.access("kr", base_t, base_t + (4 * PER - 1) * 512 + 63 * 8 + 8, "rope_k_vt Kr write")
+                buf.access("vt", base_t, base_t + (4 * PER - 1) * 512 + 63 * 8 + 8, "rope_k_vt Vt write")
     assert 2 * PREP_BLOCK * CPR * 16 <= LDS_BYTES
+    # every tile's fragments are written exactly once over the z blocks
+    assert (D // 64) * 4 * PER * 512 == PREP_BLOCK * D
 
     # attn_fwd_kernel: persistent grid of P workgroups.
     KBYTES = KBN * D * 2
