@@ -40,6 +40,7 @@ namespace regen {
 
 constexpr int kPrepKeys = 128;  // workspace padding unit (keys)
 constexpr int kPrepBlock = 64;  // keys per rope_k_vt block: one Kr / Vt tile
+constexpr int kPrepDims = 64;   // head dims per rope_k_vt block (32: 15% slower at 12 x 10920)
 constexpr int kTabLds = 3072;   // (cos, sin) entries the attention kernel keeps in LDS
 
 // Rotary geometry: latent grid, pairs per axis, offsets of each axis' table
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     int n_off, long long sh, long long sn) {
     const int hd = blockIdx.y;
     const int n0 = blockIdx.x * kPrepBlock;
-    const int z = blockIdx.z;  // head dims 64 z .. 64 z + 63 of the tile
+    const int z = blockIdx.z;  // head dims kPrepDims z .. of the tile
     const int HW = geo.H * geo.W;
 
     // Rows are staged through LDS so that both the reads of K and V (whole
@@ -133,10 +134,10 @@ __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     // blocks per tile and twice as many blocks reach the memory system at
     // D = 128 (a short call, such as three heads, does not fill the chip
     // with one block per tile).
-    constexpr int DH = 64;                // head dims per block
+    constexpr int DH = kPrepDims;         // head dims per block
     constexpr int CPR = DH / 8;           // 16-byte chunks per staged row
     constexpr int PER = kPrepBlock * CPR / 256;
-    constexpr int NF = 8;                 // 1 KiB fragments of Kr (and of Vt) per block
+    constexpr int NF = DH / 8;            // 1 KiB fragments of Kr (and of Vt) per block
     static_assert(D % DH == 0 && NF * 64 == PER * 256, "fragments per block");
     __shared__ uint4 kl[kPrepBlock * CPR];
     __shared__ uint4 vl[kPrepBlock * CPR];

@@ -547,7 +547,7 @@ regen_status enqueue(const Ctx& c, const void* q, int64_t q_begin, int64_t nq, c
     const int Npad = int((nk + regen::kPrepKeys - 1) / regen::kPrepKeys * regen::kPrepKeys);
     const float c2 = p.scale * 1.4426950408889634f;
 
-    dim3 pgrid(unsigned(Npad / regen::kPrepBlock), unsigned(p.heads), unsigned(p.head_dim / 64));
+    dim3 pgrid(unsigned(Npad / regen::kPrepBlock), unsigned(p.heads), unsigned(p.head_dim / regen::kPrepDims));
     regen::Sched sc;
     int64_t rem_tiles = 0;
     if (!make_sched(p.heads, nq, nk, c.P, &sc, &rem_tiles))
