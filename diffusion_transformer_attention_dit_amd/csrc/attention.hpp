@@ -119,8 +119,11 @@ template <int D>
 __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ kr,
     uint16_t* __restrict__ vt, const float2* __restrict__ tab, RopeGeom geo, int N, int Npad,
-    int n_off, long long sh, long long sn) {
+    int n_off, long long sh, long long sn, int* __restrict__ cnt) {
     const int hd = blockIdx.y;
+    // The attention kernel that follows on the stream claims leftover
+    // pieces from this counter.
+    if (cnt != nullptr && (blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *cnt = 0;
     const int n0 = blockIdx.x * kPrepBlock;
     const int z = blockIdx.z;  // head dims kPrepDims z .. of the tile
     const int HW = geo.H * geo.W;
@@ -245,7 +248,24 @@ struct Sched {
     int rem_units;  // units of the leftover tiles (rem * nkv)
     int rem_q;      // rem_units / Prem
     int rem_r;      // rem_units % Prem
+    int dyn;        // leftover tiles cut into pieces claimed at run time (below)
+    int ppt;        // pieces per leftover tile (dyn)
+    int npieces;    // leftover tiles x ppt (dyn)
 };
+// With dyn, the leftover tiles are not split statically: piece i (of tile
+// full P + i / ppt, key blocks [j nkv / ppt, (j + 1) nkv / ppt) for
+// j = i % ppt) goes to whichever workgroup claims it next from a counter,
+// near the end of its whole tiles. The XCDs of one GPU run at different
+// clocks, so the workgroups of the fast ones take the pieces while the slow
+// ones finish their tiles. Every piece writes partial slot i and the merge
+// folds a tile's pieces in order, so the result does not depend on which
+// workgroup took which piece.
+__host__ __device__ __forceinline__ void piece_segment(const Sched& sc, int i, int* t, int* kv0, int* kv1) {
+    const int r = i / sc.ppt, j = i - r * sc.ppt;
+    *t = sc.full * sc.P + r;
+    *kv0 = (j * sc.nkv) / sc.ppt;
+    *kv1 = ((j + 1) * sc.nkv) / sc.ppt;
+}
 // Every unit index (heads * n_qtiles * nkv) fits in 31 bits (the host checks
 // this), so the schedule runs in 32-bit integer arithmetic.
 
@@ -278,7 +298,7 @@ __host__ __device__ __forceinline__ bool get_segment(const Sched& sc, int p, int
         *kv1 = sc.nkv;
         return true;
     }
-    if (p >= sc.Prem) return false;
+    if (sc.dyn || p >= sc.Prem) return false;
     const int base = sc.full * sc.P * sc.nkv;
     const int a = base + rem_begin(sc, p), b = base + rem_begin(sc, p + 1);
     const int x = (k == sc.full) ? a : (a / sc.nkv + (k - sc.full)) * sc.nkv;
@@ -300,6 +320,7 @@ __host__ __device__ __forceinline__ bool get_segment(const Sched& sc, int p, int
 //   part_o  : [2P][BM][D] bf16 O / l of split tiles (normalised over the
 //             segment's own keys)
 //   part_ml : [2P][BM][2] fp32 (m, l) of split tiles
+//   cnt     : with sc.dyn, the piece counter, zero at entry
 // ---------------------------------------------------------------------------
 template <int D, int BN, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
@@ -308,7 +329,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float2* __restrict__ tab, RopeGeom geo, int Nq, int Nk, int Npad, int q_off,
     long long qh, long long qn_stride, long long oh, long long on_stride, Sched sc,
     float c2 /* sm_scale * log2(e) */, int rotate_q, uint16_t* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, int* __restrict__ cnt) {
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(BN == 64, "key tile: the Kr / Vt fragment layout holds 64-key tiles");
     constexpr int BM = NW * 32;
@@ -322,6 +343,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // The (cos, sin) table, when it fits: Q rows are rotated from LDS, with no
     // global load waiting behind the K / V copies in flight.
     __shared__ float2 tabsm[kTabLds];
+    __shared__ int claimed;  // the piece a workgroup claimed for its next segment
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -378,10 +400,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     int buf = 0;
     bool more = true;
 
+    int piece = -1;  // the current segment's piece (dyn leftover), else -1
     for (int k = 0; more; ++k) {
         // ---- segment k: tile t, key blocks [kv0, kv1) ----
-        int nt_ = 0, nkv0 = 0, nkv1 = 0;
-        more = get_segment(sc, pid, k + 1, &nt_, &nkv0, &nkv1);
+        int nt_ = 0, nkv0 = 0, nkv1 = 0, npiece = -1;
+        // The next segment is a claimed piece: it is claimed once this one's
+        // key blocks are done (below), so the claim reflects how far this
+        // workgroup actually got.
+        const bool next_dyn = sc.dyn && k + 1 >= sc.full;  // uniform
+        more = next_dyn ? false : get_segment(sc, pid, k + 1, &nt_, &nkv0, &nkv1);
         __amdgpu_buffer_rsrc_t nkrs = krs, nvrs = vrs;  // the next segment's head
         if (more) head_rsrc(nt_, &nkrs, &nvrs);
         const int hd = t / sc.n_qtiles, qt = t - hd * sc.n_qtiles;
@@ -616,7 +643,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             buf ^= 1;
         }
 
-        if (q_lds && more && kv1 - kv0 == 1) {
+        if (next_dyn) {
+            // Claim the next piece; its Q rows and first K/V block go to LDS
+            // now (the buffer after this segment's last block is free).
+            if (tid == 0)
+                claimed = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            npiece = claimed;
+            more = npiece < sc.npieces;
+            if (more) {
+                piece_segment(sc, npiece, &nt_, &nkv0, &nkv1);
+                head_rsrc(nt_, &nkrs, &nvrs);
+                if (q_lds) issue_q(nt_);
+                char* nks = smem + buf * (KBYTES + VBYTES);
+                issue_tile<D, BN, NW>(nkrs, nvrs, nkv0, nks, nks + KBYTES, wave, lane);
+                __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __syncthreads();
+        }
+        if (q_lds && more && kv1 - kv0 == 1 && !next_dyn) {
             // A one-block segment: copy the next Q rows now and wait.
             issue_q(nt_);
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -648,7 +693,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
         } else {
             // Part of a tile: leave (O / l in bf16, m, l) for the merge.
-            const int slot = partial_slot(sc, pid, t);
+            const int slot = piece >= 0 ? piece : partial_slot(sc, pid, t);
             const int r = wave * 32 + col;
             uint16_t* po = part_o + ((size_t)slot * BM + r) * D;
 #pragma unroll
@@ -667,6 +712,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         t = nt_;
         kv0 = nkv0;
         kv1 = nkv1;
+        piece = npiece;
         krs = nkrs;
         vrs = nvrs;
     }
@@ -697,8 +743,9 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
     constexpr int RPB = MW == 4 ? 1 : 16;     // rows per block
     const int t = sc.full * sc.P + blockIdx.x;
     const int y0 = blockIdx.x * sc.nkv;  // leftover unit offsets of tile t
-    const int p0 = rem_owner(sc, y0);
-    const int p1 = rem_owner(sc, y0 + sc.nkv - 1);
+    // Parts p0 .. p1: workgroups (static split) or pieces (dyn), in order.
+    const int p0 = sc.dyn ? blockIdx.x * sc.ppt : rem_owner(sc, y0);
+    const int p1 = sc.dyn ? p0 + sc.ppt - 1 : rem_owner(sc, y0 + sc.nkv - 1);
     if (p0 == p1) return;  // uniform over the block
     const int hd = t / sc.n_qtiles, qt = t % sc.n_qtiles;
     const int wv = threadIdx.x >> 6;
@@ -711,13 +758,13 @@ __global__ __launch_bounds__(256) void merge_kernel(uint16_t* __restrict__ o, fl
     // Partial slots: every workgroup after p0 starts its range inside tile
     // t, so t is its first leftover tile (slot 2p); p0's range starts in t
     // only if its first unit is t's first unit.
-    const int slot0 = partial_slot(sc, p0, t);
+    const int slot0 = sc.dyn ? p0 : partial_slot(sc, p0, t);
     float M = -INFINITY, L = 0.0f, acc[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
 #pragma unroll 4
     for (int p = p0 + w; p <= p1; p += MW) {
-        const int slot = p == p0 ? slot0 : 2 * p;
+        const int slot = sc.dyn ? p : (p == p0 ? slot0 : 2 * p);
         const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((size_t)slot * BM + r) * 2);
         const uint16_t* po = part_o + ((size_t)slot * BM + r) * D + lane * DPL;
         float x[DPL];

@@ -160,6 +160,7 @@ struct Slot {
     uint16_t* vt;        // transposed V, same layout
     uint16_t* part_o;    // split-tile O / l, bf16 [2P][BM][D]
     float* part_ml;      // split-tile (m, l)      [2P][BM][2]
+    int* cnt;            // leftover piece counter (zeroed by the K pass)
     uint16_t* qkv;       // attention blocks only: projection output [N][3 hidden]
     uint16_t* attn_out;  // attention blocks only: attention output  [N][hidden]
     hipEvent_t done;     // recorded after the last kernel of every call using the slot
@@ -168,6 +169,7 @@ struct Slot {
     uint64_t stamp;      // order of last use
 };
 constexpr int kSlots = 2;
+constexpr int kPieceBlocks = 6;  // key blocks per claimed leftover piece (at least)
 
 struct regen_attn {
     int device;
@@ -209,8 +211,8 @@ void free_handle(regen_attn* h) {
         if (sl.done && sl.used) (void)hipEventSynchronize(sl.done);
     if (h->d_tab) (void)hipFree(h->d_tab);
     for (Slot& sl : h->slot) {
-        for (void* ptr : {(void*)sl.kr, (void*)sl.vt, (void*)sl.part_o, (void*)sl.part_ml, (void*)sl.qkv,
-                          (void*)sl.attn_out})
+        for (void* ptr : {(void*)sl.kr, (void*)sl.vt, (void*)sl.part_o, (void*)sl.part_ml, (void*)sl.cnt,
+                          (void*)sl.qkv, (void*)sl.attn_out})
             if (ptr) (void)hipFree(ptr);
         if (sl.done) (void)hipEventDestroy(sl.done);
     }
@@ -355,6 +357,7 @@ regen_status regen_attn_create(const regen_attn_desc* desc, regen_attn_t* out) {
         if (e == hipSuccess) e = hipMalloc(&sl.vt, half_ws);
         if (e == hipSuccess) e = hipMalloc(&sl.part_o, part_o_bytes);
         if (e == hipSuccess) e = hipMalloc(&sl.part_ml, part_ml_bytes);
+        if (e == hipSuccess) e = hipMalloc(&sl.cnt, sizeof(int));
         if (e == hipSuccess) e = hipEventCreateWithFlags(&sl.done, hipEventDisableTiming);
     }
     if (e != hipSuccess) {
@@ -403,6 +406,7 @@ struct Ctx {
     uint16_t* vt;
     uint16_t* part_o;
     float* part_ml;
+    int* cnt;
 };
 
 regen_status enqueue(const Ctx& c, const void* q, int64_t q_begin, int64_t nq, const void* k,
@@ -455,7 +459,7 @@ Strides caller_strides(const Problem& p, int64_t nq, int64_t nk) {
 
 Ctx handle_ctx(const regen_attn* h, const Slot* sl) {
     return Ctx{&h->p, &h->geo, h->d_tab, h->d_tab_id, h->P, h->Pc, sl->kr, sl->vt, sl->part_o,
-               sl->part_ml};
+               sl->part_ml, sl->cnt};
 }
 
 // One profiling record of handle h (h->mu held), or NULL for an unprofiled handle.
@@ -533,6 +537,22 @@ bool make_sched(int heads, int64_t nq, int64_t nk, int P, regen::Sched* sc, int6
     sc->Prem = sc->rem_units < P ? (sc->rem_units > 0 ? sc->rem_units : 1) : P;
     sc->rem_q = sc->rem_units / sc->Prem;
     sc->rem_r = sc->rem_units % sc->Prem;
+    // A small leftover after whole-tile passes (at most 8 key blocks per
+    // workgroup) is cut into pieces of at least kPieceBlocks key blocks that
+    // workgroups claim as they finish, at most 2P of them (one partial slot
+    // each). Pieces of 3 / 6 / 12 blocks measured 618.8 / 616.3 / 615.5 us
+    // per 12 x 10920 call against 628.0 for the static split; larger pieces
+    // cost more where the XCDs' clocks happen to agree.
+    sc->dyn = 0;
+    sc->ppt = 1;
+    sc->npieces = 0;
+    if (sc->full >= 1 && *rem_tiles > 0 && sc->rem_units <= int64_t(8) * P) {
+        const int64_t ppt =
+            std::min<int64_t>(std::max<int64_t>(nkv / kPieceBlocks, 1), 2 * int64_t(P) / *rem_tiles);
+        sc->dyn = 1;
+        sc->ppt = int(ppt);
+        sc->npieces = int(*rem_tiles * ppt);
+    }
     return true;
 }
 
@@ -555,7 +575,7 @@ regen_status enqueue(const Ctx& c, const void* q, int64_t q_begin, int64_t nq, c
                     "too many (query tile, key block) pairs for one call (heads * ceil(q/256) * "
                     "ceil(k/64) must stay below 2^31)");
     // Tiles split many ways merge with 4 waves per row, others with one.
-    const bool mw4 = sc.Prem >= 8 * rem_tiles;
+    const bool mw4 = sc.dyn ? sc.ppt >= 8 : sc.Prem >= 8 * rem_tiles;
     const dim3 mgrid{unsigned(rem_tiles), unsigned(mw4 ? kBM : kBM / 16), 1u};
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
     const uint16_t* k16 = static_cast<const uint16_t*>(k);
@@ -601,11 +621,11 @@ regen_status enqueue(const Ctx& c, const void* q, int64_t q_begin, int64_t nq, c
         mark(2);
     } else if (p.head_dim == 128) {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<128>, pgrid, dim3(256), 0, st, k16, v16, c.kr,
-                           c.vt, tab, geo, Nk, Npad, k_off, kh, kn);
+                           c.vt, tab, geo, Nk, Npad, k_off, kh, kn, sc.dyn ? c.cnt : nullptr);
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<128, kBN, kNW>), dim3(c.P), dim3(kNW * 64), 0,
                            st, q16, c.kr, c.vt, o16, lse, tab, geo, Nq, Nk, Npad,
-                           q_off, qh, qn, oh, on, sc, c2, int(!cross), c.part_o, c.part_ml);
+                           q_off, qh, qn, oh, on, sc, c2, int(!cross), c.part_o, c.part_ml, c.cnt);
         mark(2);
         if (rem_tiles > 0) {
             if (mw4)
@@ -617,11 +637,11 @@ regen_status enqueue(const Ctx& c, const void* q, int64_t q_begin, int64_t nq, c
         }
     } else {
         hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, c.kr,
-                           c.vt, tab, geo, Nk, Npad, k_off, kh, kn);
+                           c.vt, tab, geo, Nk, Npad, k_off, kh, kn, sc.dyn ? c.cnt : nullptr);
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<64, kBN, kNW>), dim3(c.P), dim3(kNW * 64), 0,
                            st, q16, c.kr, c.vt, o16, lse, tab, geo, Nq, Nk, Npad,
-                           q_off, qh, qn, oh, on, sc, c2, int(!cross), c.part_o, c.part_ml);
+                           q_off, qh, qn, oh, on, sc, c2, int(!cross), c.part_o, c.part_ml, c.cnt);
         mark(2);
         if (rem_tiles > 0) {
             if (mw4)
@@ -1131,14 +1151,15 @@ regen_status regen_attn_forward_noalloc(const regen_attn_desc* desc, const void*
     regen::RopeGeom geo;
     const int64_t entries = rope_geometry(p, &geo);
     const int P = int(std::min<int64_t>(sd.slots[hsel], p.units));
-    // Scratch layout: table | Kr | Vt | partial O / l | partial (m, l), each
-    // at a 256-byte boundary.
+    // Scratch layout: table | Kr | Vt | partial O / l | partial (m, l) | piece
+    // counter, each at a 256-byte boundary.
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t tab_b = up(size_t(entries) * sizeof(float2));
     const size_t half_ws = up(workspace_bytes(p) / 2);
     const size_t po_b = up(size_t(2) * P * kBM * p.head_dim * sizeof(uint16_t));
     const size_t pm_b = up(size_t(2) * P * kBM * 2 * sizeof(float));
-    const size_t need = tab_b + 2 * half_ws + po_b + pm_b;
+    const size_t cnt_b = up(sizeof(int));
+    const size_t need = tab_b + 2 * half_ws + po_b + pm_b + cnt_b;
     if (entries >= (int64_t(1) << 31) || need > REGEN_NOALLOC_SCRATCH_BYTES)
         return fail(REGEN_ERR_UNSUPPORTED,
                     "problem needs " + std::to_string(need) + " bytes of scratch; the allocation-free "
@@ -1152,7 +1173,8 @@ regen_status regen_attn_forward_noalloc(const regen_attn_desc* desc, const void*
           reinterpret_cast<uint16_t*>(base + tab_b),
           reinterpret_cast<uint16_t*>(base + tab_b + half_ws),
           reinterpret_cast<uint16_t*>(base + tab_b + 2 * half_ws),
-          reinterpret_cast<float*>(base + tab_b + 2 * half_ws + po_b)};
+          reinterpret_cast<float*>(base + tab_b + 2 * half_ws + po_b),
+          reinterpret_cast<int*>(base + tab_b + 2 * half_ws + po_b + pm_b)};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(regen::rope_table_kernel, dim3(unsigned((entries + 255) / 256)), dim3(256), 0, st, tab,
                        geo, p.base, int(!(p.flags & REGEN_ATTN_NO_ROPE)), int(entries));

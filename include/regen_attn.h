@@ -115,7 +115,8 @@ typedef struct regen_attn *regen_attn_t;
  * area for query tiles whose keys are split over several workgroups of the
  * persistent attention kernel: 2 * P * 256 * (2 * head_dim + 8) bytes (bf16
  * O/l and fp32 (m, l) per row), P = resident workgroups of the device (one
- * per compute unit on MI355X: 33 MiB at head_dim 128).
+ * per compute unit on MI355X: 33 MiB at head_dim 128), plus a 4-byte counter
+ * of the leftover pieces workgroups claim.
  * On success *out receives the handle; on any failure *out is set to NULL
  * (when out is not NULL) and the status says why:
  *   INVALID_ARGUMENT (NULL desc/out, wrong struct_size, heads/grid < 1,
@@ -134,9 +135,13 @@ regen_status regen_attn_create(const regen_attn_desc *desc, regen_attn_t *out);
  * device pointers to contiguous bf16 [heads][tokens][head_dim] tensors,
  * 16-byte aligned; o must not overlap q, k or v. The buffer sizes cannot be
  * checked from raw pointers: each must hold heads * tokens * head_dim bf16
- * values. Errors: INVALID_ARGUMENT (NULL or destroyed handle, NULL or
- * misaligned pointer, o overlapping an input), HIP (launch failure; detail
- * in regen_attn_last_error). Faults during execution surface at the
+ * values. The same inputs give bit-identical outputs on every call: query
+ * tiles whose keys are split over workgroups are cut at fixed key blocks and
+ * merged in a fixed order, whichever workgroup computed a part (workgroups
+ * claim the last parts as they finish, since the device's parts do not all
+ * run at one clock). Errors: INVALID_ARGUMENT (NULL or destroyed handle,
+ * NULL or misaligned pointer, o overlapping an input), HIP (launch failure;
+ * detail in regen_attn_last_error). Faults during execution surface at the
  * caller's next synchronization.
  */
 regen_status regen_attn_forward(regen_attn_t h, const void *q, const void *k,
@@ -299,7 +304,7 @@ regen_status regen_attn_destroy(regen_attn_t h);
  * looks its address up. Problems that need more than that (the table, 2 *
  * heads * ceil(tokens/128)*128 * head_dim * 2 bytes of workspace and
  * 2 * P * 256 * (2 * head_dim + 8) bytes of partials, P = resident
- * workgroups) are rejected with UNSUPPORTED: the 25-frame window (12 x 10920
+ * workgroups, and a piece counter, each at a 256-byte boundary) are rejected with UNSUPPORTED: the 25-frame window (12 x 10920
  * x 128, about 102 MB) fits, the 77-frame clip (12 x 31200 x 128) does not.
  * Every call on a device shares its one array, and each call leaves its
  * contents behind: calls that overlap in time on one device (different

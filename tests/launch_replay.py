@@ -21,6 +21,7 @@ import numpy as np
 KBM, KBN, KNW = 256, 64, 8          # attention: query rows per tile, keys per block, waves
 PREP_KEYS, PREP_BLOCK = 128, 64     # workspace padding unit, keys per rope_k_vt block
 TAB_LDS = 3072                      # (cos, sin) entries attn_fwd_kernel keeps in LDS
+PIECE_BLOCKS = 6                    # key blocks per claimed leftover piece (at least)
 GEMM_TILE, GEMM_BK, GEMM_BIG = 128, 64, 256
 LDS_BYTES = 160 * 1024
 
@@ -63,8 +64,19 @@ def make_sched(heads, nq, nk, P):
     rem_tiles = tiles - full * P
     rem_units = rem_tiles * nkv
     Prem = (rem_units if rem_units > 0 else 1) if rem_units < P else P
-    return dict(n_qtiles=n_qtiles, nkv=nkv, P=P, full=full, Prem=Prem, rem_units=rem_units,
-                rem_q=rem_units // Prem, rem_r=rem_units % Prem, rem_tiles=rem_tiles)
+    sc = dict(n_qtiles=n_qtiles, nkv=nkv, P=P, full=full, Prem=Prem, rem_units=rem_units,
+              rem_q=rem_units // Prem, rem_r=rem_units % Prem, rem_tiles=rem_tiles, dyn=0, ppt=1, npieces=0)
+    # a small leftover after whole-tile passes: pieces claimed at run time
+    if full >= 1 and rem_tiles > 0 and rem_units <= 8 * P:
+        ppt = min(max(nkv // PIECE_BLOCKS, 1), 2 * P // rem_tiles)
+        sc.update(dyn=1, ppt=ppt, npieces=rem_tiles * ppt)
+    return sc
+
+
+def piece_segment(sc, i):
+    r, j = divmod(i, sc["ppt"])
+    return (i32(sc["full"] * sc["P"] + r), i32(j * sc["nkv"]) // sc["ppt"],
+            i32((j + 1) * sc["nkv"]) // sc["ppt"])
 
 
 def i32(x):
@@ -90,7 +102,7 @@ def partial_slot(sc, p, t):
 def get_segment(sc, p, k):
     if k < sc["full"]:
         return i32(k * sc["P"] + p), 0, sc["nkv"]
-    if p >= sc["Prem"]:
+    if sc["dyn"] or p >= sc["Prem"]:
         return None
     nkv = sc["nkv"]
     base = i32(sc["full"] * sc["P"] * nkv)
@@ -199,6 +211,17 @@ def attention_call(buf, *, heads, D, nq, nk, tokens_pad, P, q_name, q_base, qh, 
                 slots[key] = t
                 buf.access("part_o", slot * BM * D, (slot * BM + BM) * D, "attn partial O")
                 buf.access("part_ml", slot * BM * 2, (slot * BM + BM) * 2, "attn partial (m, l)")
+    # Claimed pieces (any workgroup may take any piece; each writes slot i).
+    for i in range(sc["npieces"]):
+        t, kv0, kv1 = piece_segment(sc, i)
+        assert 0 <= kv0 < kv1 <= sc["nkv"] and kv1 - kv0 >= min(PIECE_BLOCKS, sc["nkv"])
+        covered[t, kv0:kv1] += 1
+        if not i < 2 * P:
+            raise OutOfBounds("piece %d has no partial slot (2P = %d)" % (i, 2 * P))
+        if not (kv0 == 0 and kv1 == sc["nkv"]):
+            buf.access("part_o", i * BM * D, (i * BM + BM) * D, "attn partial O (piece)")
+            buf.access("part_ml", i * BM * 2, (i * BM + BM) * 2, "attn partial (m, l) (piece)")
+            slots[("piece", i)] = t
     if not np.all(covered == 1):
         raise OutOfBounds("schedule does not cover every (tile, key block) exactly once")
 
@@ -206,6 +229,20 @@ def attention_call(buf, *, heads, D, nq, nk, tokens_pad, P, q_name, q_base, qh, 
     # kernel wrote, writes O (and lse) of split tiles.
     for bx in range(sc["rem_tiles"]):
         t = sc["full"] * P + bx
+        if sc["dyn"]:
+            if sc["ppt"] == 1:
+                continue
+            for i in range(bx * sc["ppt"], (bx + 1) * sc["ppt"]):
+                if slots.get(("piece", i)) != t:
+                    raise OutOfBounds("merge reads piece slot %d, which holds no part of tile %d" % (i, t))
+            h, qt = t // sc["n_qtiles"], t % sc["n_qtiles"]
+            rows = min(BM, nq - qt * BM)
+            r = np.arange(qt * BM, qt * BM + rows, dtype=np.int64)
+            ooff = o_base + h * oh + r * on
+            buf.access(o_name, ooff.min(), ooff.max() + D, "merge O store")
+            if lse:
+                buf.access("lse", h * nq + r.min(), h * nq + r.max() + 1, "merge lse store")
+            continue
         y0 = bx * sc["nkv"]
         p0, p1 = rem_owner(sc, y0), rem_owner(sc, y0 + sc["nkv"] - 1)
         if p0 == p1:

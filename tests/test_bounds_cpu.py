@@ -104,6 +104,28 @@ def test_replay_detects_planted_overrun():
                          o_name="o", o_base=0, oh=w.head_dim, on=hid)
 
 
+def test_claimed_pieces_where_the_leftover_is_small():
+    """Whole-tile passes followed by a leftover of at most 8 key blocks per
+    workgroup use claimed pieces (the 25-frame window); no whole-tile pass
+    (3-head share, 1560 tokens) or a large leftover (77-frame clip) keep the
+    static split. Pieces cover the leftover tiles exactly and fit 2P slots."""
+    assert R.make_sched(12, 10920, 10920, 256)["dyn"] == 1
+    for heads, n in ((3, 10920), (12, 1560), (12, 31200)):
+        assert R.make_sched(heads, n, n, 256)["dyn"] == 0
+    for heads, n, P in ((12, 10920, 256), (12, 5400, 256), (12, 10920, 240), (1, 65536, 64)):
+        sc = R.make_sched(heads, n, n, P)
+        if not sc["dyn"]:
+            continue
+        assert sc["npieces"] <= 2 * P
+        covered = {}
+        for i in range(sc["npieces"]):
+            t, kv0, kv1 = R.piece_segment(sc, i)
+            for b in range(kv0, kv1):
+                assert (t, b) not in covered
+                covered[(t, b)] = i
+        assert len(covered) == sc["rem_tiles"] * sc["nkv"]
+
+
 def test_schedule_replay_matches_closed_forms():
     """The leftover ranges partition the leftover units: rem_begin is
     floor(p * units / Prem) for every p, and rem_owner inverts it."""
