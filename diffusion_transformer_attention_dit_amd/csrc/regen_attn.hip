@@ -542,11 +542,15 @@ bool make_sched(int heads, int64_t nq, int64_t nk, int P, regen::Sched* sc, int6
     // workgroups claim as they finish, at most 2P of them (one partial slot
     // each). Pieces of 3 / 6 / 12 blocks measured 618.8 / 616.3 / 615.5 us
     // per 12 x 10920 call against 628.0 for the static split; larger pieces
-    // cost more where the XCDs' clocks happen to agree.
+    // cost more where the XCDs' clocks happen to agree. Only for long key
+    // runs (at least 16 pieces' worth per tile): with short ones a workgroup's
+    // whole share is a few blocks, the clocks' spread is a fraction of a
+    // block, and a claimed piece costs more than the static split (512 keys:
+    // 51 -> 59 us).
     sc->dyn = 0;
     sc->ppt = 1;
     sc->npieces = 0;
-    if (sc->full >= 1 && *rem_tiles > 0 && sc->rem_units <= int64_t(8) * P) {
+    if (sc->full >= 1 && *rem_tiles > 0 && sc->rem_units <= int64_t(8) * P && nkv >= 16 * kPieceBlocks) {
         const int64_t ppt =
             std::min<int64_t>(std::max<int64_t>(nkv / kPieceBlocks, 1), 2 * int64_t(P) / *rem_tiles);
         sc->dyn = 1;

@@ -67,7 +67,7 @@ def make_sched(heads, nq, nk, P):
     sc = dict(n_qtiles=n_qtiles, nkv=nkv, P=P, full=full, Prem=Prem, rem_units=rem_units,
               rem_q=rem_units // Prem, rem_r=rem_units % Prem, rem_tiles=rem_tiles, dyn=0, ppt=1, npieces=0)
     # a small leftover after whole-tile passes: pieces claimed at run time
-    if full >= 1 and rem_tiles > 0 and rem_units <= 8 * P:
+    if full >= 1 and rem_tiles > 0 and rem_units <= 8 * P and nkv >= 16 * PIECE_BLOCKS:
         ppt = min(max(nkv // PIECE_BLOCKS, 1), 2 * P // rem_tiles)
         sc.update(dyn=1, ppt=ppt, npieces=rem_tiles * ppt)
     return sc

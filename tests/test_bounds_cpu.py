@@ -112,7 +112,9 @@ def test_claimed_pieces_where_the_leftover_is_small():
     assert R.make_sched(12, 10920, 10920, 256)["dyn"] == 1
     for heads, n in ((3, 10920), (12, 1560), (12, 31200)):
         assert R.make_sched(heads, n, n, 256)["dyn"] == 0
-    for heads, n, P in ((12, 10920, 256), (12, 5400, 256), (12, 10920, 240), (1, 65536, 64)):
+    # short key runs (a 512-token cross-attention context) keep the static split
+    assert R.make_sched(12, 10920, 512, 256)["dyn"] == 0
+    for heads, n, P in ((12, 10920, 256), (2, 32800, 256), (12, 6400, 256), (12, 10920, 240)):
         sc = R.make_sched(heads, n, n, P)
         if not sc["dyn"]:
             continue
@@ -124,6 +126,8 @@ def test_claimed_pieces_where_the_leftover_is_small():
                 assert (t, b) not in covered
                 covered[(t, b)] = i
         assert len(covered) == sc["rem_tiles"] * sc["nkv"]
+    assert R.make_sched(2, 32800, 32800, 256)["dyn"] == 1
+    R.attention_forward(2, 128, 32800, 256)  # every access of that call in bounds
 
 
 def test_schedule_replay_matches_closed_forms():
