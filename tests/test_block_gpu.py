@@ -76,16 +76,44 @@ def test_linear_against_fp64(rows, fin, fout):
     assert err.sum() / np.abs(ref).sum() <= 3e-3
 
 
+@pytest.mark.parametrize("rows,fin,fout", [
+    # persistent kernel: 11 x 36 = 396 tiles of 256 x 256, one round on 256
+    # CUs, the other 140 as 560 quarters taken in turn, ragged last tile row
+    # (2600 = 10 x 256 + 40)
+    (2600, 64, 9216),
+    # 16 x 24 = 384 tiles: one round, 128 tiles as 512 quarters
+    (4096, 128, 6144),
+])
+def test_linear_every_element_written(rows, fin, fout):
+    say("case linear (output prefilled with NaN) rows=%d in=%d out=%d" % (rows, fin, fout))
+    g = torch.Generator().manual_seed(rows + fin + fout)
+    x = torch.randn(rows, fin, generator=g).to(torch.bfloat16)
+    w = (torch.randn(fout, fin, generator=g) * fin ** -0.5).to(torch.bfloat16)
+    out = torch.full((rows, fout), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):  # the second call overwrites the first one's output
+        y = native.linear(x.cuda(), w.cuda(), out=out)
+    torch.cuda.synchronize()
+    ref = x.double().numpy() @ w.double().numpy().T
+    got = f64(y)
+    assert np.all(np.isfinite(got)), "elements left unwritten"
+    err = np.abs(got - ref)
+    assert err.max() <= 2 ** -8 * np.abs(ref).max() + 1e-4, err.max()
+    assert err.sum() / np.abs(ref).sum() <= 3e-3
+
+
 def test_linear_window_qkv_shape_sampled_rows():
     # The QKV projection at the 25-frame window's size (10920 x 1536 -> 4608:
-    # 3096 tiles, 24 of them as quarter tiles), checked on sampled rows.
+    # 43 x 18 = 774 tiles of 256 x 256, three rounds and 6 tiles as eighths),
+    # every element written, sampled rows checked against fp64.
     rows, fin, fout = 10920, 1536, 4608
     say("case linear rows=%d in=%d out=%d (sampled rows)" % (rows, fin, fout))
     g = torch.Generator().manual_seed(11)
     x = torch.randn(rows, fin, generator=g).to(torch.bfloat16)
     w = (torch.randn(fout, fin, generator=g) * fin ** -0.5).to(torch.bfloat16)
-    y = native.linear(x.cuda(), w.cuda())
+    out = torch.full((rows, fout), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = native.linear(x.cuda(), w.cuda(), out=out)
     torch.cuda.synchronize()
+    assert not torch.isnan(y).any().item(), "elements left unwritten"
     pick = synth.sample_rows(rows, 384, seed=3)
     ref = x.double().numpy()[pick] @ w.double().numpy().T
     got = f64(y)[pick]

@@ -73,7 +73,7 @@ def test_block_in_bounds(name, slots):
 @pytest.mark.parametrize("rows,fin,fout", [
     (1, 64, 1), (37, 64, 100), (128, 128, 128), (1000, 256, 129), (300, 1536, 4608),
     (1560, 1536, 4608), (10920, 1536, 1536), (10920, 1536, 4608), (4100, 256, 2000),
-    (4100, 256, 4100),
+    (4100, 256, 4100), (2600, 64, 9216), (4096, 128, 6144),
 ])
 def test_gemm_in_bounds_and_covered(rows, fin, fout):
     buf = R.Buffers(x=rows * fin, w=fout * fin, y=rows * fout)
