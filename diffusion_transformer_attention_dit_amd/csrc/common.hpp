@@ -30,6 +30,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
 // in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 left at their maximum).
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// ... and for lgkmcnt <= n only (vmcnt and expcnt at their maximum).
+constexpr int lgkmcnt_only(int n) { return 15 | (3 << 14) | (7 << 4) | ((n & 15) << 8); }
 
 // Logical block id with consecutive ids on one XCD. Blocks are dispatched
 // round-robin over the 8 XCDs (block b runs on XCD b % 8); this maps each

@@ -152,7 +152,9 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* __restrict
 // 128 x 64 eighths (32 x 32 per wave) when they fit in one round, else as
 // 128 x 128 quarters (32 x 64 per wave), quarter q to workgroup q mod G.
 // Tiles are numbered in groups of 4 tile rows as in gemm_nt_kernel, and the
-// workgroups of one XCD take consecutive numbers.
+// workgroups of one XCD take consecutive numbers. A tile's C goes out
+// through LDS in whole rows (16-byte chunks, a row of a wave's block per 8
+// or 16 lanes) wherever the tile lies within N and rows are 16-byte aligned.
 // ---------------------------------------------------------------------------
 constexpr int kGemmBig = 256;
 constexpr int kGemmBigSmem = 2 * 2 * kGemmBig * kGemmBK * 2;  // [buffer][A, B] at 256 rows
@@ -256,6 +258,44 @@ __device__ __forceinline__ void gemm8_tile(__amdgpu_buffer_rsrc_t ra, int lda, _
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
+    }
+    if (n0 + TN <= N && (ldc & 7) == 0) {  // uniform
+        // C through LDS (free now: every wave is past its last operand
+        // read): each wave writes its WTM x WTN block in bf16 row-major into
+        // its own part of smem (16-byte chunks XOR-swizzled by row), reads
+        // it back as whole row chunks and stores it so that each store
+        // instruction writes whole rows (at WTN = 128 two 128-byte lines
+        // per row). The L2 then takes whole lines rather than 8-byte pieces
+        // from 32 rows per instruction, which made writing C cost about
+        // twice as much.
+        constexpr int CPR = WTN / 8, RPI = 64 / CPR;  // 16-byte chunks per row, rows per store
+        static_assert(8 * WTM * WTN * 2 <= kGemmBigSmem && RPI * CPR == 64, "C staging");
+        char* ws = smem + wave * (WTM * WTN * 2);
+#pragma unroll
+        for (int i = 0; i < NBM; ++i)
+#pragma unroll
+            for (int j = 0; j < NBN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int r = i * 32 + col, c = j * 4 + g;
+                    const f32x16& v = acc[i][j];
+                    *reinterpret_cast<uint2*>(ws + r * (WTN * 2) + (c ^ (r & (CPR - 1))) * 16 + half * 8) =
+                        make_uint2(pack_bf16(v[g * 4], v[g * 4 + 1]), pack_bf16(v[g * 4 + 2], v[g * 4 + 3]));
+                }
+        // A wave's LDS accesses complete in order: its reads below see its
+        // writes above.
+#pragma unroll
+        for (int k = 0; k < WTM / RPI; ++k) {
+            const int r = k * RPI + lane / CPR, c = lane % CPR;
+            const uint4 x = *reinterpret_cast<const uint4*>(ws + r * (WTN * 2) + (c ^ (r & (CPR - 1))) * 16);
+            const int m = m0 + wm * WTM + r;
+            if (m < M) *reinterpret_cast<uint4*>(C + (long long)m * ldc + n0 + wn * WTN + c * 8) = x;
+        }
+        // Every wave is done reading smem before the next tile's copies
+        // refill it (the stores need not have completed: no vmcnt wait).
+        __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));
+        __builtin_amdgcn_s_barrier();
+        return;
     }
     const bool st8 = (ldc & 3) == 0;
 #pragma unroll
