@@ -75,8 +75,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // outside the resource, so loads return zero and stores are dropped
     // without touching memory. The counts of memory operations between two
     // points are then fixed, and each wait below names exactly what it needs.
-    constexpr int QL = D / 16;                 // Q loads per unit
-    constexpr int ST = D / 8 + (LSE ? 1 : 0);  // stores per unit
+    constexpr int QL = D / 16;  // Q loads per unit
+    // O of a unit goes out through LDS as whole rows when the context leaves
+    // room past it for every wave's 32 x D block (contexts of up to 128 keys),
+    // else straight from the accumulators in 8-byte pieces of 32 rows, which
+    // the memory side takes at a higher cost. Stores per unit either way:
+    constexpr int OROW = D * 2 + 16;                             // LDS bytes per staged O row (padded)
+    constexpr int OBYTES = 32 * OROW;                            // a unit's O block in LDS
+    constexpr int ST_ROWS = 32 * D * 2 / 1024 + (LSE ? 1 : 0);   // 16 bytes per lane
+    constexpr int ST_PIECES = D / 8 + (LSE ? 1 : 0);             // 8 bytes per lane
+    static_assert(NW * OBYTES <= (kCrossMaxKeys / BN) * TBYTES, "O staging area");
+    const bool o_lds = nkv * TBYTES + NW * OBYTES <= (kCrossMaxKeys / BN) * TBYTES;  // uniform
     constexpr uint32_t kOut = 0x80000000u;     // past every resource (the host keeps them < 2^31 bytes)
     const uint32_t q_bytes = (uint32_t)(((long long)(Nq - 1) * qn_stride + D) * 2);
     const uint32_t o_bytes = (uint32_t)(((long long)(Nq - 1) * on_stride + D) * 2);
@@ -212,16 +221,49 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                                    false);
         const float l_row = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         const float inv = 1.0f / l_row;
-        const uint32_t ooff = qrow < Nq ? (uint32_t)(((long long)qrow * on_stride + half * 4) * 2) : kOut;
+        if (o_lds) {
+            // This wave's block of the LDS area past the context: O written
+            // in the accumulator layout (rows padded by 16 bytes, so that the
+            // 32 rows of one write spread over the banks while every address
+            // stays a lane base plus a constant), read back as whole rows
+            // (the wave's LDS accesses complete in order) and stored CPR
+            // lanes per row.
+            constexpr int CPR = D / 8, RPI = 64 / CPR;
+            char* ws = smem + (kCrossMaxKeys / BN) * TBYTES - (NW - wave) * OBYTES;
+            char* wl = ws + col * OROW + half * 8;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 w2 = {pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv),
-                                  pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv)};
-                __builtin_amdgcn_raw_buffer_store_b64(w2, ors, ooff + (db * 32 + g4 * 8) * 2, 0, 0);
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    uint2 w2;
+                    w2.x = pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv);
+                    w2.y = pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv);
+                    *reinterpret_cast<uint2*>(wl + (db * 4 + g4) * 16) = w2;
+                }
+            const int row0 = qrow - col;
+            const char* rl = ws + (lane / CPR) * OROW + (lane % CPR) * 16;
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int r = k * RPI + lane / CPR, c = lane % CPR;
+                const uint4 x = *reinterpret_cast<const uint4*>(rl + k * RPI * OROW);
+                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 w4 = {x.x, x.y, x.z, x.w};
+                const uint32_t off =
+                    row0 + r < Nq ? (uint32_t)(((long long)(row0 + r) * on_stride + c * 8) * 2) : kOut;
+                __builtin_amdgcn_raw_buffer_store_b128(w4, ors, off, 0, 0);
             }
+        } else {
+            const uint32_t ooff = qrow < Nq ? (uint32_t)(((long long)qrow * on_stride + half * 4) * 2) : kOut;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2 w2 = {pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv),
+                                      pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv)};
+                    __builtin_amdgcn_raw_buffer_store_b64(w2, ors, ooff + (db * 32 + g4 * 8) * 2, 0, 0);
+                }
+        }
         if (LSE) {
             const uint32_t loff = (qrow < Nq && half == 0) ? (uint32_t)qrow * 4 : kOut;
             __builtin_amdgcn_raw_buffer_store_b32(
@@ -312,12 +354,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (; u < seg_end; u += 2 * NW) {
             bf16x8 qf[D / 16];
             if (first) __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_only(ST));
+            else if (o_lds) __builtin_amdgcn_s_waitcnt(vmcnt_only(ST_ROWS));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_only(ST_PIECES));
             scale_q(qa, qf);
             load_q(qb, qrs, h, u + NW, seg_end);
             unit(qf, ors, lrs, h, u);
             if (u + NW >= seg_end) break;
-            __builtin_amdgcn_s_waitcnt(vmcnt_only(ST));
+            if (o_lds) __builtin_amdgcn_s_waitcnt(vmcnt_only(ST_ROWS));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_only(ST_PIECES));
             scale_q(qb, qf);
             load_q(qa, qrs, h, u + 2 * NW, seg_end);
             unit(qf, ors, lrs, h, u + NW);

@@ -39,7 +39,7 @@ def check_o(got, ref, label):
 # 1..256 run in the short-context kernel (up to 128 with its O rows staged
 # through LDS; 256: eight full key tiles), 257 and
 # up in the persistent one.
-@pytest.mark.parametrize("ctx_len", [1, 64, 77, 128, 129, 226, 256, 257, 512, 1000])
+@pytest.mark.parametrize("ctx_len", [1, 64, 77, 96, 97, 128, 129, 226, 256, 257, 512, 1000])
 def test_cross_block_all_elements(ctx_len):
     w = synth.WORKLOADS["block_12x128_n1560"]
     say("case cross-attention block, ctx %d" % ctx_len)
