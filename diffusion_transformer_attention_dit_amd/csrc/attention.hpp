@@ -203,6 +203,34 @@ __global__ __launch_bounds__(256) void rope_k_vt_kernel(
     }
 }
 
+// Rows of O from the P V accumulators of one wave: acc[db] holds O^T for 32
+// head dims x 32 rows, lane (col, half) having row col's head dims
+// 32 db + 8 g + 4 half .. + 3 (g < 4). Each pair of 8-dim chunks (2 gp,
+// 2 gp + 1) is exchanged with lane ^ 32 (two v_permlane32_swap), so that
+// lane (col, half) ends up with all 8 dims of chunk 2 gp + 1 - half and
+// stores 16 bytes: a store instruction writes 32 contiguous bytes of each of
+// the 32 rows rather than 16, which the memory side takes at less cost.
+// put(d0, w) stores the 16 bytes w at head dim d0 of this lane's row; every
+// lane of the wave must take part (the swaps read lane ^ 32).
+template <int D, typename Put>
+__device__ __forceinline__ void store_o_rows(const f32x16 (&acc)[D / 32], float scale, int half, Put&& put) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            const int g = 2 * gp;
+            const uint32_t a0 = pack_bf16(acc[db][g * 4 + 0] * scale, acc[db][g * 4 + 1] * scale);
+            const uint32_t a1 = pack_bf16(acc[db][g * 4 + 2] * scale, acc[db][g * 4 + 3] * scale);
+            const uint32_t b0 = pack_bf16(acc[db][g * 4 + 4] * scale, acc[db][g * 4 + 5] * scale);
+            const uint32_t b1 = pack_bf16(acc[db][g * 4 + 6] * scale, acc[db][g * 4 + 7] * scale);
+            // [0]: b with lanes 32.. taken from a of lanes ..31; [1]: a with
+            // lanes ..31 taken from b of lanes 32..
+            const auto s0 = __builtin_amdgcn_permlane32_swap(b0, a0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(b1, a1, false, false);
+            put(db * 32 + (g + 1 - half) * 8, make_uint4(s0[0], s1[0], s0[1], s1[1]));
+        }
+}
+
 // Issue the copies of K tile j and Vt tile j into LDS buffer (ks, vs). Both
 // are stored in HBM as runs of 1 KiB MFMA operand fragments in lane order,
 // which land unchanged in LDS: run r of a tile goes to byte 1024 r of the
@@ -676,36 +704,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const float inv = 1.0f / l_row;
         if (kv0 == 0 && kv1 == sc.nkv) {
             // Whole tile here: O = O^T / l, bf16; lse = ln 2 (m + log2 l).
+            // Both lanes of a row (col, 0 / 1) are active together.
             if (qrow < Nq) {
                 if (lse != nullptr && half == 0)
                     lse[(size_t)hd * Nq + qrow] = (m_run + log2f(l_row)) * 0.69314718055994531f;
                 uint16_t* op = o + hd * oh + qrow * on_stride;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int d0 = db * 32 + g4 * 8 + half * 4;
-                        uint2 w2;
-                        w2.x = pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv);
-                        w2.y = pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv);
-                        *reinterpret_cast<uint2*>(op + d0) = w2;
-                    }
+                store_o_rows<D>(acc, inv, half,
+                                [&](int d0, uint4 w) { *reinterpret_cast<uint4*>(op + d0) = w; });
             }
         } else {
             // Part of a tile: leave (O / l in bf16, m, l) for the merge.
             const int slot = piece >= 0 ? piece : partial_slot(sc, pid, t);
             const int r = wave * 32 + col;
             uint16_t* po = part_o + ((size_t)slot * BM + r) * D;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int d0 = db * 32 + g4 * 8 + half * 4;
-                    uint2 w2;
-                    w2.x = pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv);
-                    w2.y = pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv);
-                    *reinterpret_cast<uint2*>(po + d0) = w2;
-                }
+            store_o_rows<D>(acc, inv, half, [&](int d0, uint4 w) { *reinterpret_cast<uint4*>(po + d0) = w; });
             if (half == 0)
                 *reinterpret_cast<float2*>(part_ml + ((size_t)slot * BM + r) * 2) = make_float2(m_run, l_row);
         }

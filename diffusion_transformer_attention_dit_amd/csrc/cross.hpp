@@ -77,13 +77,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // points are then fixed, and each wait below names exactly what it needs.
     constexpr int QL = D / 16;  // Q loads per unit
     // O of a unit goes out through LDS as whole rows when the context leaves
-    // room past it for every wave's 32 x D block (contexts of up to 128 keys),
-    // else straight from the accumulators in 8-byte pieces of 32 rows, which
-    // the memory side takes at a higher cost. Stores per unit either way:
-    constexpr int OROW = D * 2 + 16;                             // LDS bytes per staged O row (padded)
-    constexpr int OBYTES = 32 * OROW;                            // a unit's O block in LDS
-    constexpr int ST_ROWS = 32 * D * 2 / 1024 + (LSE ? 1 : 0);   // 16 bytes per lane
-    constexpr int ST_PIECES = D / 8 + (LSE ? 1 : 0);             // 8 bytes per lane
+    // room past it for every wave's 32 x D block (head_dim 128: contexts of
+    // up to 96 keys), else from the accumulators as 32 bytes of each of the
+    // 32 rows per store (store_o_rows), which the memory side takes at a
+    // higher cost. Either way a unit's O is D / 16 stores of 16 bytes per lane.
+    constexpr int OROW = D * 2 + 16;   // LDS bytes per staged O row (padded)
+    constexpr int OBYTES = 32 * OROW;  // a unit's O block in LDS
+    constexpr int ST = D / 16 + (LSE ? 1 : 0);  // stores per unit
+    static_assert(32 * D * 2 / 1024 == D / 16, "stores per unit on both paths");
     static_assert(NW * OBYTES <= (kCrossMaxKeys / BN) * TBYTES, "O staging area");
     const bool o_lds = nkv * TBYTES + NW * OBYTES <= (kCrossMaxKeys / BN) * TBYTES;  // uniform
     constexpr uint32_t kOut = 0x80000000u;     // past every resource (the host keeps them < 2^31 bytes)
@@ -253,16 +254,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 __builtin_amdgcn_raw_buffer_store_b128(w4, ors, off, 0, 0);
             }
         } else {
-            const uint32_t ooff = qrow < Nq ? (uint32_t)(((long long)qrow * on_stride + half * 4) * 2) : kOut;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                    const u32x2 w2 = {pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv),
-                                      pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv)};
-                    __builtin_amdgcn_raw_buffer_store_b64(w2, ors, ooff + (db * 32 + g4 * 8) * 2, 0, 0);
-                }
+            const uint32_t ooff = qrow < Nq ? (uint32_t)((long long)qrow * on_stride * 2) : kOut;
+            store_o_rows<D>(acc, inv, half, [&](int d0, uint4 w) {
+                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 w4 = {w.x, w.y, w.z, w.w};
+                __builtin_amdgcn_raw_buffer_store_b128(w4, ors, ooff + d0 * 2, 0, 0);
+            });
         }
         if (LSE) {
             const uint32_t loff = (qrow < Nq && half == 0) ? (uint32_t)qrow * 4 : kOut;
@@ -354,14 +351,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (; u < seg_end; u += 2 * NW) {
             bf16x8 qf[D / 16];
             if (first) __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-            else if (o_lds) __builtin_amdgcn_s_waitcnt(vmcnt_only(ST_ROWS));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_only(ST_PIECES));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_only(ST));
             scale_q(qa, qf);
             load_q(qb, qrs, h, u + NW, seg_end);
             unit(qf, ors, lrs, h, u);
             if (u + NW >= seg_end) break;
-            if (o_lds) __builtin_amdgcn_s_waitcnt(vmcnt_only(ST_ROWS));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_only(ST_PIECES));
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(ST));
             scale_q(qb, qf);
             load_q(qa, qrs, h, u + 2 * NW, seg_end);
             unit(qf, ors, lrs, h, u + NW);
