@@ -445,7 +445,7 @@ def clip_window_leg(reps=1):
 # the window bench; its stdout JSON line in trace/bench.json), fetch / write
 # (--pmc FETCH_SIZE / WRITE_SIZE of one window), calf / calw (the same
 # counters over --copy-calibration-mib 512), sq1, sq2 (instruction and cycle
-# counters of one window); commands.txt holds the commands, one per line.
+# counters of one window); commands*.txt hold the commands, one per line.
 # Any other subdirectory with a kernel trace gets a duration table.
 # ---------------------------------------------------------------------------
 
@@ -525,9 +525,9 @@ def summarize_rocprof(run_dir, out_dir, workload="window25_12x128_n10920"):
     w = synth.WORKLOADS[workload]
     os.makedirs(out_dir, exist_ok=True)
     cmds = []
-    cpath = os.path.join(run_dir, "commands.txt")
-    if os.path.exists(cpath):
-        cmds = [c.rstrip("\n") for c in open(cpath) if c.strip()]
+    for cname in sorted(os.listdir(run_dir)):  # commands.txt, commands_*.txt (one per GPU session)
+        if cname.startswith("commands") and cname.endswith(".txt"):
+            cmds += [c.rstrip("\n") for c in open(os.path.join(run_dir, cname)) if c.strip()]
     L = ["# Kernel profile: 3D-RoPE attention, %s (%d heads x %d tokens x head_dim %d, bf16)"
          % (w.name, w.heads, w.tokens, w.head_dim), "",
          "Measured on one MI355X (gfx950) with rocprofv3, each pass its own run of the committed "
