@@ -649,19 +649,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     if (c + RING < NV) fr[(NK + c) % RING] = frag(NK + vfrag(c + RING));
                 }
             }
-#ifdef REGEN_PV_HINTS
-            // Issue order: group 0's P, then each product followed by a share
-            // of the next group's P and one operand read.
-            __builtin_amdgcn_sched_group_barrier(0x402, 16, 0);
-#pragma unroll
-            for (int c = 0; c < NV - DB; ++c) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x402, 16 / DB, 0);
-                if constexpr (NV > RING) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int c = 0; c < DB; ++c) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#endif
 
             // The next block's copies must have landed (this wave's: vmcnt;
             // the others': the barrier) before anyone reads them, and every
