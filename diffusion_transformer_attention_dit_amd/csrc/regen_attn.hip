@@ -572,6 +572,8 @@ regen_status enqueue(const Ctx& c, const void* q, int64_t q_begin, int64_t nq, c
     const float c2 = p.scale * 1.4426950408889634f;
 
     dim3 pgrid(unsigned(Npad / regen::kPrepBlock), unsigned(p.heads), unsigned(p.head_dim / regen::kPrepDims));
+    // A K pass of fewer than 8 blocks per CU stores nontemporally.
+    const bool kp_nt = int64_t(pgrid.x) * pgrid.y * pgrid.z < int64_t(8) * c.P;
     regen::Sched sc;
     int64_t rem_tiles = 0;
     if (!make_sched(p.heads, nq, nk, c.P, &sc, &rem_tiles))
@@ -624,8 +626,12 @@ regen_status enqueue(const Ctx& c, const void* q, int64_t q_begin, int64_t nq, c
         }
         mark(2);
     } else if (p.head_dim == 128) {
-        hipLaunchKernelGGL(regen::rope_k_vt_kernel<128>, pgrid, dim3(256), 0, st, k16, v16, c.kr,
-                           c.vt, tab, geo, Nk, Npad, k_off, kh, kn, sc.dyn ? c.cnt : nullptr);
+        if (kp_nt)
+            hipLaunchKernelGGL((regen::rope_k_vt_kernel<128, true>), pgrid, dim3(256), 0, st, k16, v16, c.kr,
+                               c.vt, tab, geo, Nk, Npad, k_off, kh, kn, sc.dyn ? c.cnt : nullptr);
+        else
+            hipLaunchKernelGGL((regen::rope_k_vt_kernel<128, false>), pgrid, dim3(256), 0, st, k16, v16, c.kr,
+                               c.vt, tab, geo, Nk, Npad, k_off, kh, kn, sc.dyn ? c.cnt : nullptr);
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<128, kBN, kNW>), dim3(c.P), dim3(kNW * 64), 0,
                            st, q16, c.kr, c.vt, o16, lse, tab, geo, Nq, Nk, Npad,
@@ -640,7 +646,7 @@ regen_status enqueue(const Ctx& c, const void* q, int64_t q_begin, int64_t nq, c
                                    lse, c.part_o, c.part_ml, Nq, sc, oh, on);
         }
     } else {
-        hipLaunchKernelGGL(regen::rope_k_vt_kernel<64>, pgrid, dim3(256), 0, st, k16, v16, c.kr,
+        hipLaunchKernelGGL((regen::rope_k_vt_kernel<64, false>), pgrid, dim3(256), 0, st, k16, v16, c.kr,
                            c.vt, tab, geo, Nk, Npad, k_off, kh, kn, sc.dyn ? c.cnt : nullptr);
         mark(1);
         hipLaunchKernelGGL((regen::attn_fwd_kernel<64, kBN, kNW>), dim3(c.P), dim3(kNW * 64), 0,
