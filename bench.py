@@ -223,7 +223,8 @@ def block_leg(w, reps=10):
     xw = torch.randn(window.tokens, hid, generator=g, device="cuda").to(torch.bfloat16)
     wq = (torch.randn(3 * hid, hid, generator=g, device="cuda") * hid ** -0.5).to(torch.bfloat16)
     yq = torch.empty(window.tokens, 3 * hid, dtype=torch.bfloat16, device="cuda")
-    native.linear(xw, wq, out=yq, stream=stream)
+    for _ in range(5):  # warm-up
+        native.linear(xw, wq, out=yq, stream=stream)
     torch.cuda.synchronize()
     a.record(stream)
     for _ in range(reps):
@@ -235,7 +236,8 @@ def block_leg(w, reps=10):
     # The output projection alone at the window's token count.
     wo = (torch.randn(hid, hid, generator=g, device="cuda") * hid ** -0.5).to(torch.bfloat16)
     yo = torch.empty(window.tokens, hid, dtype=torch.bfloat16, device="cuda")
-    native.linear(xw, wo, out=yo, stream=stream)
+    for _ in range(5):  # warm-up
+        native.linear(xw, wo, out=yo, stream=stream)
     torch.cuda.synchronize()
     a.record(stream)
     for _ in range(reps):
